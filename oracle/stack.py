@@ -1,0 +1,201 @@
+"""Oracle stack compositions, float64 numpy.  Test infrastructure only.
+
+``oracle_forward`` evaluates one workload candidate by candidate on the dense
+early-fused model: the request features are copied into every candidate's
+state row (materialized broadcast), every layer runs on that dense row with
+masked weights, and request outputs are read back from the request part of
+each candidate's row.  Requests never share work with each other, so any
+subset of requests can be evaluated on its own.
+
+The request-only sequence encoder of the DCA workloads reads no candidate
+input at all ([R] §2.2, first equation), so it is evaluated once per
+request; its keys and values are then copied per candidate (K~ = K[m],
+V~ = V[m]) before attention.
+
+Compositions (the pages fix the operators, not these stacks):
+  glm_tiny  one GLM linear, group-local LayerNorm, ReLU
+  glm_mlp   blocks x <- RMSNorm_g(x + GLMLin(ReLU(GLMLin(x)))), then a
+            scalar GLM head (d_out_r = 0, d_out_c = 1)
+  dca       per interaction layer: [LCB + ReLU], ReLU(GLMLin), GLMLin = G
+            (the query), A = Attn(G, K/V of encoder output S_src(i)),
+            next state [G || A] per group; optional scalar head
+  wukong    masked FM, token-axis LCB, u = [vec F || vec T] per group,
+            h1 = LN_g(ReLU(GLMLin u)), h2 = LN_g(h1 + ReLU(GLMLin h1)),
+            scalar head
+Parity of the glm_tiny/glm_mlp/dca(one layer) compositions is pinned by
+the invariance and building-block tests; the wukong and multi-depth dca
+compositions are "parity unpinned" as compositions (their operators are
+pinned individually).
+"""
+
+from __future__ import annotations
+
+from typing import Any, Dict, Optional
+
+import numpy as np
+
+from . import ops
+
+F64 = np.float64
+
+
+def _rows_for(inputs: Dict[str, Any], requests) -> tuple:
+    """Candidate rows of the chosen requests plus a dummy row for each empty request.
+
+    The dummy candidate (zero features) is legal because request outputs
+    do not depend on candidate inputs ([R] §2.1, two-group form).
+    Returns (row_index_or_-1, request_of_row).
+    """
+    cand2req = np.asarray(inputs["cand2req"])
+    B = inputs["cfg"].B
+    reqs = np.arange(B) if requests is None else np.asarray(requests)
+    keep = np.isin(cand2req, reqs)
+    rows = np.nonzero(keep)[0]
+    req_of = cand2req[rows].astype(np.int64)
+    have = set(req_of.tolist())
+    dummies = [b for b in reqs.tolist() if b not in have]
+    rows = np.concatenate([rows, -np.ones(len(dummies), dtype=np.int64)])
+    req_of = np.concatenate([req_of, np.asarray(dummies, dtype=np.int64)])
+    return rows, req_of, reqs
+
+
+def oracle_encoder(inputs: Dict[str, Any], requests=None) -> Dict[str, Any]:
+    """Request-only encoder outputs S_0..S_n_enc and per-depth K/V projections.
+
+    [R] §2.2: S_k = Enc_k(S_{k-1}) per request; K = S W_K, V = S W_V for the
+    request and candidate query groups at each interaction depth (no bias).
+    Returns {"S": [S_0..], "kv": [(K_R, V_R, K_C, V_C) per depth]} indexed by
+    request id (rows of requests not asked for are left zero).
+    """
+    cfg = inputs["cfg"]
+    w = inputs["w"]
+    B = cfg.B
+    reqs = np.arange(B) if requests is None else np.asarray(requests)
+    S0 = np.zeros((B,) + inputs["seq"].shape[1:], dtype=F64)
+    S0[reqs] = inputs["seq"][reqs]
+    Ss = [S0]
+    for k in range(cfg.n_enc):
+        p = {nm: w[f"enc{k}.{nm}"] for nm in ("w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2")}
+        Sk = np.zeros_like(S0)
+        Sk[reqs] = ops.encoder_layer(Ss[-1][reqs], p, cfg.n_heads, cfg.eps)
+        Ss.append(Sk)
+    kv = []
+    for i, src in enumerate(cfg.depth_src()):
+        S = Ss[src]
+        kv.append(tuple(S @ np.asarray(w[f"kv{i}.{nm}"], F64).T for nm in ("wk_r", "wv_r", "wk_c", "wv_c")))
+    return {"S": Ss, "kv": kv}
+
+
+def _forward_rows(cfg, w, x_r_rows, x_c_rows, req_of, enc) -> Dict[str, np.ndarray]:
+    """Run the dense model on a chunk of candidate rows; returns the final state and logits."""
+    H = cfg.hidden
+    if cfg.kind == "glm_tiny":
+        x = np.concatenate([x_r_rows, x_c_rows], axis=1)
+        y = ops.glm_linear(x, w["lin.W"], w["lin.b"], cfg.d_r, H)
+        y = ops.relu(ops.group_norm(y, [H, H], "layer", cfg.eps))
+        return {"y": y, "w_r": H, "logits": None}
+
+    if cfg.kind == "glm_mlp":
+        x = np.concatenate([x_r_rows, x_c_rows], axis=1)
+        for k in range(cfg.n_blocks):
+            h = ops.relu(ops.glm_linear(x, w[f"blk{k}.up.W"], w[f"blk{k}.up.b"], cfg.d_r, H))
+            o = ops.glm_linear(h, w[f"blk{k}.down.W"], w[f"blk{k}.down.b"], H, cfg.d_r)
+            x = ops.group_norm(x + o, [cfg.d_r, cfg.d_c], "rms", cfg.eps)
+        logits = ops.glm_linear(x, w["head.W"], w["head.b"], cfg.d_r, 0)[:, 0]
+        return {"y": x, "w_r": cfg.d_r, "logits": logits}
+
+    if cfg.kind == "dca":
+        d = cfg.d_seq
+        x = np.concatenate([x_r_rows, x_c_rows], axis=1)
+        din_r = cfg.d_r
+        for i in range(cfg.n_int):
+            if cfg.qgen_lcb:
+                x = ops.relu(ops.glm_linear(x, w[f"int{i}.lcb.W"], w[f"int{i}.lcb.b"], din_r, din_r))
+            h = ops.relu(ops.glm_linear(x, w[f"int{i}.mlp1.W"], w[f"int{i}.mlp1.b"], din_r, H))
+            g = ops.glm_linear(h, w[f"int{i}.mlp2.W"], w[f"int{i}.mlp2.b"], H, d)
+            g_r, g_c = g[:, :d], g[:, d:]
+            KR, VR, KC, VC = enc["kv"][i]
+            a_r = np.empty_like(g_r)
+            a_c = np.empty_like(g_c)
+            L = KR.shape[1]
+            step = max(1, (1 << 27) // (L * d * 8 * 4))
+            for s in range(0, len(req_of), step):
+                m = req_of[s:s + step]
+                # materialized broadcast of the request's keys/values to each candidate
+                a_r[s:s + step] = ops.attention(g_r[s:s + step, None, :], KR[m], VR[m], cfg.n_heads)[:, 0]
+                a_c[s:s + step] = ops.attention(g_c[s:s + step, None, :], KC[m], VC[m], cfg.n_heads)[:, 0]
+            x = np.concatenate([g_r, a_r, g_c, a_c], axis=1)
+            din_r = 2 * d
+        logits = None
+        if cfg.head:
+            logits = ops.glm_linear(x, w["head.W"], w["head.b"], din_r, 0)[:, 0]
+        return {"y": x, "w_r": din_r, "logits": logits}
+
+    if cfg.kind == "wukong":
+        nr, T = cfg.n_tok_r, cfg.tok_out
+        X = np.concatenate([x_r_rows, x_c_rows], axis=1)  # [n, nr + nc, D]
+        f_r, f_c = ops.masked_fm(X, nr)
+        t_r, t_c = ops.token_lcb(X, w["tok.W"], nr, T)
+        u = np.concatenate([f_r, t_r, f_c, t_c], axis=1)
+        u_r = f_r.shape[1] + t_r.shape[1]
+        h1 = ops.group_norm(ops.relu(ops.glm_linear(u, w["mlp1.W"], w["mlp1.b"], u_r, H)), [H, H], "layer", cfg.eps)
+        h2 = ops.relu(ops.glm_linear(h1, w["mlp2.W"], w["mlp2.b"], H, H))
+        h2 = ops.group_norm(h1 + h2, [H, H], "layer", cfg.eps)
+        logits = ops.glm_linear(h2, w["head.W"], w["head.b"], H, 0)[:, 0]
+        return {"y": h2, "w_r": H, "logits": logits}
+
+    raise ValueError(cfg.kind)
+
+
+def oracle_forward(inputs: Dict[str, Any], requests=None, chunk: int = 1024) -> Dict[str, Any]:
+    """Dense per-candidate evaluation of one workload.
+
+    requests: optional subset of request ids (all candidates of each chosen
+    request are evaluated).  Returns
+      rows      candidate row indices (into the input's candidate arrays)
+      y_c       [len(rows), w_c] final candidate-group state
+      logits    [len(rows)] scalar scores, or None
+      requests  the chosen request ids
+      y_r       [len(requests), w_r] request-group state, read from the
+                request's candidates; every candidate must agree
+                ([R] §2.1, request-output equality)
+    """
+    cfg = inputs["cfg"]
+    w = inputs["w"]
+    rows, req_of, reqs = _rows_for(inputs, requests)
+    enc = oracle_encoder(inputs, reqs) if cfg.kind == "dca" else None
+
+    x_r = np.asarray(inputs["x_r"], dtype=F64)
+    x_c = np.asarray(inputs["x_c"], dtype=F64)
+    ys, logits = [], []
+    w_r = None
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        m = req_of[s:s + chunk]
+        xr_rows = x_r[m]  # materialized broadcast of request features
+        xc_rows = np.where((r >= 0).reshape((-1,) + (1,) * (x_c.ndim - 1)), x_c[np.maximum(r, 0)], 0.0)
+        out = _forward_rows(cfg, w, xr_rows, xc_rows, m, enc)
+        ys.append(out["y"])
+        w_r = out["w_r"]
+        if out["logits"] is not None:
+            logits.append(out["logits"])
+    y = np.concatenate(ys, axis=0) if ys else np.zeros((0, 0))
+
+    real = rows >= 0
+    y_r = np.zeros((len(reqs), w_r), dtype=F64)
+    for j, b in enumerate(reqs.tolist()):
+        sel = y[req_of == b, :w_r]
+        ref = sel[0]
+        spread = np.max(np.abs(sel - ref)) if len(sel) > 1 else 0.0
+        tol = 1e-12 * max(1.0, float(np.max(np.abs(ref))))
+        if spread > tol:
+            raise AssertionError(f"request {b}: request outputs differ across its candidates by {spread}")
+        y_r[j] = ref
+    res = {
+        "rows": rows[real],
+        "requests": reqs,
+        "y_r": y_r,
+        "y_c": y[real, w_r:],
+        "logits": np.concatenate(logits)[real] if logits else None,
+    }
+    return res

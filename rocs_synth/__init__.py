@@ -1,0 +1,311 @@
+"""Seeded synthetic inputs for the ROCS shared-forward stack.
+
+This module is the only code shared by the CPU oracle (``oracle/``) and the
+HIP path (``request_candidate_sharing_amd``).  It draws random numbers and
+lays out the ragged request/candidate batch; it contains none of the method's
+arithmetic (no linear maps, norms, interactions or attention).
+
+Workload shapes follow the five stack configurations of the ROCS problem
+statement (liuzhao09.github.io ROCS review, section 2 "method" for the
+operators; the workload sizes themselves are the benchmark's own).  Every
+reading of an unstated detail (variance notation, fan-in, count
+distributions, which encoder depth feeds which interaction layer) is applied
+here once and documented with the configuration.
+
+Conventions
+-----------
+* N(0, v): the second parameter is a variance, so N(0, 1/fan_in) draws with
+  standard deviation fan_in**-0.5.
+* fan_in of a GLM linear layer is the full dense input width d_in_r + d_in_c.
+* A dense GLM weight is drawn as one ``[d_out_r + d_out_c, d_in_r + d_in_c]``
+  matrix.  Its request-output x candidate-input block is drawn like the rest
+  and left in place: zeroing it is the operator's job (the mask), not the
+  generator's.
+* bf16 workloads round every drawn array once, fp32 -> bf16 with
+  round-to-nearest-even, and return float32 arrays holding bf16 values.
+* Draw order: counts -> x_r -> x_c -> sequence -> weights in layer order.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Any, Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "StackConfig",
+    "config",
+    "small_config",
+    "make_inputs",
+    "make_batch",
+    "shuffle_candidates",
+    "round_bf16",
+    "glm_weight",
+    "CONFIG_NAMES",
+]
+
+CONFIG_NAMES = {
+    1: "tiny GLM check (fp32)",
+    2: "GLM MLP stack (bf16)",
+    3: "DCA sequence block (bf16)",
+    4: "Wukong-style ROCSified interaction layer (bf16)",
+    5: "ranking-scale full stack (bf16)",
+}
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even).
+
+    Returns float32 values that are exactly representable in bf16.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(a.shape)
+
+
+@dataclasses.dataclass(frozen=True)
+class StackConfig:
+    """Shape description of one workload.
+
+    kind is one of ``glm_tiny`` (config 1), ``glm_mlp`` (config 2),
+    ``dca`` (configs 3 and 5) and ``wukong`` (config 4).
+    """
+
+    key: int
+    kind: str
+    dtype: str  # "f32" or "bf16"
+    B: int
+    counts: tuple  # ("uniform", lo, hi) | ("fixed", n) | ("lognormal", median, sigma, lo, hi)
+    d_r: int = 0
+    d_c: int = 0
+    hidden: int = 0  # per-group hidden width of the GLM MLPs
+    n_blocks: int = 0  # glm_mlp: residual MLP blocks
+    # DCA
+    L: int = 0
+    d_seq: int = 0
+    n_heads: int = 0
+    head_dim: int = 64
+    ffn: int = 0
+    n_enc: int = 0
+    n_int: int = 0
+    qgen_lcb: bool = False  # config 3: an LCB (GLM linear + ReLU) in front of the query MLP
+    head: bool = True
+    # Wukong-style tokens
+    n_tok_r: int = 0
+    n_tok_c: int = 0
+    tok_dim: int = 0
+    tok_out: int = 0  # tokens per group after the token-axis LCB
+    x_var: float = 1.0
+    eps: float = 1e-5
+
+    def name(self) -> str:
+        return CONFIG_NAMES.get(self.key, self.kind)
+
+    def with_(self, **kw) -> "StackConfig":
+        return dataclasses.replace(self, **kw)
+
+    def depth_src(self) -> list:
+        """Encoder output S_k read by interaction layer i (1-based k).
+
+        Layer i of n_int reads S_ceil(i * n_enc / n_int): with two encoder
+        layers and one interaction layer that is S_2; with four interaction
+        layers it is S_1, S_1, S_2, S_2.  The pages pair depth i with S_i
+        (ROCS review, section 2.2, the DCA encoder/cross-attention equations)
+        but leave unequal depth counts open.
+        """
+        return [int(math.ceil(i * self.n_enc / self.n_int)) for i in range(1, self.n_int + 1)]
+
+    def to_dict(self) -> Dict[str, Any]:
+        return dataclasses.asdict(self)
+
+
+def config(k: int) -> StackConfig:
+    """The five benchmark workloads at full size."""
+    if k == 1:
+        return StackConfig(key=1, kind="glm_tiny", dtype="f32", B=4, counts=("uniform", 1, 16),
+                           d_r=32, d_c=32, hidden=32, head=False)
+    if k == 2:
+        return StackConfig(key=2, kind="glm_mlp", dtype="bf16", B=256, counts=("uniform", 64, 512),
+                           d_r=512, d_c=512, hidden=1024, n_blocks=3, head=True)
+    if k == 3:
+        return StackConfig(key=3, kind="dca", dtype="bf16", B=64, counts=("fixed", 500),
+                           d_r=256, d_c=256, hidden=1024, L=256, d_seq=256, n_heads=4, head_dim=64,
+                           ffn=1024, n_enc=2, n_int=1, qgen_lcb=True, head=False)
+    if k == 4:
+        return StackConfig(key=4, kind="wukong", dtype="bf16", B=128,
+                           counts=("lognormal", 200.0, 0.5, 16, 1024),
+                           n_tok_r=32, n_tok_c=16, tok_dim=128, tok_out=64, hidden=1024,
+                           x_var=0.1, head=True)
+    if k == 5:
+        return StackConfig(key=5, kind="dca", dtype="bf16", B=32,
+                           counts=("lognormal", 1000.0, math.log(1.3), 700, 1300),
+                           d_r=512, d_c=512, hidden=2048, L=1024, d_seq=512, n_heads=8, head_dim=64,
+                           ffn=2048, n_enc=2, n_int=4, qgen_lcb=False, head=True)
+    raise ValueError(f"no configuration {k}")
+
+
+def small_config(k: int) -> StackConfig:
+    """Reduced variants of each workload for CPU-oracle parity at every tile path.
+
+    Same composition and dtype as the full configuration, sizes cut so the
+    float64 oracle finishes in about a second while the GPU kernels still
+    see several tiles per dimension and ragged tails.
+    """
+    c = config(k)
+    if k == 1:
+        return c
+    if k == 2:
+        return c.with_(B=12, counts=("uniform", 0, 150), d_r=136, d_c=72, hidden=200, n_blocks=2)
+    if k == 3:
+        return c.with_(B=5, counts=("uniform", 0, 140), d_r=128, d_c=64, hidden=256, L=200, d_seq=128,
+                       n_heads=2, ffn=512, n_enc=2, n_int=1)
+    if k == 4:
+        return c.with_(B=6, counts=("uniform", 0, 90), n_tok_r=8, n_tok_c=4, tok_dim=64, tok_out=16,
+                       hidden=256)
+    if k == 5:
+        return c.with_(B=4, counts=("uniform", 1, 120), d_r=128, d_c=64, hidden=256, L=136, d_seq=128,
+                       n_heads=2, ffn=256, n_enc=2, n_int=3)
+    raise ValueError(k)
+
+
+def _draw_counts(rng: np.random.Generator, cfg: StackConfig) -> np.ndarray:
+    spec = cfg.counts
+    if spec[0] == "uniform":
+        return rng.integers(spec[1], spec[2] + 1, cfg.B).astype(np.int64)
+    if spec[0] == "fixed":
+        return np.full(cfg.B, int(spec[1]), dtype=np.int64)
+    if spec[0] == "lognormal":
+        median, sigma, lo, hi = spec[1:]
+        z = rng.standard_normal(cfg.B)
+        return np.clip(np.rint(median * np.exp(sigma * z)), lo, hi).astype(np.int64)
+    raise ValueError(spec)
+
+
+def make_batch(counts) -> Dict[str, np.ndarray]:
+    """Ragged batch descriptor from per-request candidate counts.
+
+    Candidates are stored contiguously per request: request b owns rows
+    offsets[b] .. offsets[b+1]-1 and cand2req maps each row to its request.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    offsets = np.zeros(len(counts) + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    cand2req = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return {"counts": counts, "offsets": offsets, "cand2req": cand2req}
+
+
+def _normal(rng, shape, var, bf16):
+    a = (rng.standard_normal(shape, dtype=np.float32) * np.float32(math.sqrt(var))).astype(np.float32)
+    return round_bf16(a) if bf16 else a
+
+
+def glm_weight(rng, d_in_r, d_in_c, d_out_r, d_out_c, bf16, fan_in=None):
+    """Dense [d_out_r + d_out_c, d_in_r + d_in_c] weight drawn from N(0, 1/fan_in)."""
+    fan_in = fan_in if fan_in is not None else (d_in_r + d_in_c)
+    return _normal(rng, (d_out_r + d_out_c, d_in_r + d_in_c), 1.0 / fan_in, bf16)
+
+
+def make_inputs(cfg: StackConfig, seed: Optional[int] = None, counts=None) -> Dict[str, Any]:
+    """Draw one batch and one set of weights for ``cfg``.
+
+    seed defaults to 100 + cfg.key.  ``counts`` overrides the drawn
+    per-request candidate counts (the draw still happens so that the rest of
+    the stream is unchanged).
+    """
+    seed = 100 + cfg.key if seed is None else seed
+    rng = np.random.default_rng(seed)
+    bf16 = cfg.dtype == "bf16"
+    drawn = _draw_counts(rng, cfg)
+    if counts is not None:
+        drawn = np.asarray(counts, dtype=np.int64)
+        assert len(drawn) == cfg.B
+    out: Dict[str, Any] = {"cfg": cfg, "seed": seed}
+    out.update(make_batch(drawn))
+    Bc = int(drawn.sum())
+    w: Dict[str, np.ndarray] = {}
+    out["w"] = w
+
+    if cfg.kind in ("glm_tiny", "glm_mlp", "dca"):
+        out["x_r"] = _normal(rng, (cfg.B, cfg.d_r), cfg.x_var, bf16)
+        out["x_c"] = _normal(rng, (Bc, cfg.d_c), cfg.x_var, bf16)
+    elif cfg.kind == "wukong":
+        out["x_r"] = _normal(rng, (cfg.B, cfg.n_tok_r, cfg.tok_dim), cfg.x_var, bf16)
+        out["x_c"] = _normal(rng, (Bc, cfg.n_tok_c, cfg.tok_dim), cfg.x_var, bf16)
+    if cfg.kind == "dca":
+        out["seq"] = _normal(rng, (cfg.B, cfg.L, cfg.d_seq), 1.0, bf16)
+
+    zeros = lambda n: np.zeros(n, dtype=np.float32)
+
+    if cfg.kind == "glm_tiny":
+        w["lin.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, cfg.hidden, cfg.hidden, bf16)
+        w["lin.b"] = zeros(2 * cfg.hidden)
+    elif cfg.kind == "glm_mlp":
+        for k in range(cfg.n_blocks):
+            w[f"blk{k}.up.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, cfg.hidden, cfg.hidden, bf16)
+            w[f"blk{k}.up.b"] = zeros(2 * cfg.hidden)
+            w[f"blk{k}.down.W"] = glm_weight(rng, cfg.hidden, cfg.hidden, cfg.d_r, cfg.d_c, bf16)
+            w[f"blk{k}.down.b"] = zeros(cfg.d_r + cfg.d_c)
+        w["head.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, 0, 1, bf16)
+        w["head.b"] = zeros(1)
+    elif cfg.kind == "dca":
+        d, f = cfg.d_seq, cfg.ffn
+        for k in range(cfg.n_enc):
+            w[f"enc{k}.w_qkv"] = _normal(rng, (3 * d, d), 1.0 / d, bf16)
+            w[f"enc{k}.b_qkv"] = zeros(3 * d)
+            w[f"enc{k}.w_o"] = _normal(rng, (d, d), 1.0 / d, bf16)
+            w[f"enc{k}.b_o"] = zeros(d)
+            w[f"enc{k}.w_1"] = _normal(rng, (f, d), 1.0 / d, bf16)
+            w[f"enc{k}.b_1"] = zeros(f)
+            w[f"enc{k}.w_2"] = _normal(rng, (d, f), 1.0 / f, bf16)
+            w[f"enc{k}.b_2"] = zeros(d)
+        din_r, din_c = cfg.d_r, cfg.d_c
+        for i in range(cfg.n_int):
+            for nm in ("wk_r", "wv_r", "wk_c", "wv_c"):
+                w[f"kv{i}.{nm}"] = _normal(rng, (d, d), 1.0 / d, bf16)
+            if cfg.qgen_lcb:
+                w[f"int{i}.lcb.W"] = glm_weight(rng, din_r, din_c, din_r, din_c, bf16)
+                w[f"int{i}.lcb.b"] = zeros(din_r + din_c)
+            w[f"int{i}.mlp1.W"] = glm_weight(rng, din_r, din_c, cfg.hidden, cfg.hidden, bf16)
+            w[f"int{i}.mlp1.b"] = zeros(2 * cfg.hidden)
+            w[f"int{i}.mlp2.W"] = glm_weight(rng, cfg.hidden, cfg.hidden, d, d, bf16)
+            w[f"int{i}.mlp2.b"] = zeros(2 * d)
+            din_r, din_c = 2 * d, 2 * d  # next layer reads [G || A]
+        if cfg.head:
+            w["head.W"] = glm_weight(rng, din_r, din_c, 0, 1, bf16)
+            w["head.b"] = zeros(1)
+    elif cfg.kind == "wukong":
+        nr, nc, D, T, H = cfg.n_tok_r, cfg.n_tok_c, cfg.tok_dim, cfg.tok_out, cfg.hidden
+        w["tok.W"] = glm_weight(rng, nr, nc, T, T, bf16)
+        u_r = nr * nr + T * D
+        u_c = nc * (nr + nc) + T * D
+        w["mlp1.W"] = glm_weight(rng, u_r, u_c, H, H, bf16)
+        w["mlp1.b"] = zeros(2 * H)
+        w["mlp2.W"] = glm_weight(rng, H, H, H, H, bf16)
+        w["mlp2.b"] = zeros(2 * H)
+        w["head.W"] = glm_weight(rng, H, H, 0, 1, bf16)
+        w["head.b"] = zeros(1)
+    else:
+        raise ValueError(cfg.kind)
+    return out
+
+
+def shuffle_candidates(inputs: Dict[str, Any], seed: int = 7) -> Dict[str, Any]:
+    """Same batch with candidate rows in a random global order.
+
+    Returns a shallow copy whose candidate arrays and cand2req are permuted
+    and whose offsets are None (candidates no longer contiguous per
+    request); ``perm`` maps new row j to old row perm[j].
+    """
+    rng = np.random.default_rng(seed)
+    Bc = len(inputs["cand2req"])
+    perm = rng.permutation(Bc)
+    out = dict(inputs)
+    out["perm"] = perm
+    out["cand2req"] = np.ascontiguousarray(inputs["cand2req"][perm])
+    out["x_c"] = np.ascontiguousarray(inputs["x_c"][perm])
+    out["offsets"] = None
+    return out
