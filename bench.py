@@ -1,0 +1,239 @@
+"""Throughput of the ROCS shared forward stack on one MI355X.
+
+One step = one rocs_stack_forward over one batch of the GLM MLP stack workload
+(B = 256 requests, N_b ~ U{64..512} candidates, d_R = d_C = 512, three GLM
+MLP blocks of hidden 1024 per group with residual and group-local RMSNorm,
+scalar head; bf16 storage, fp32 accumulation), inputs resident in HBM.
+
+Prints one JSON line: candidates/s, MFMA utilisation, the same-GPU
+dense-broadcast comparator and its speedup, the roofline of the dominant
+kernel (the IKBO candidate GEMM, timed with HIP events on its launch
+stream) and the CPU oracle's rate on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15  # dense MFMA bf16, FLOP/s
+PEAK_HBM = 8.0e12   # bytes/s
+METRIC = "candidates/sec through ROCS layer stack, MFMA util %, speedup vs dense broadcast"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def glm_mlp_work(cfg, B_r, B_c):
+    """Algorithmic FLOPs and bytes of one shared-execution step (request side once, candidate side per candidate)."""
+    d, H = cfg.d_r, cfg.hidden
+    F = 0.0
+    Bts = 0.0
+    for _ in range(cfg.n_blocks):
+        # up: [B_r x 2H] = x_r [W_RR; W_CR]^T ; candidates: [B_c x H] from d
+        F += 2.0 * B_r * (2 * H) * d + 2.0 * B_c * H * d
+        # down: [B_r x 2d] from H ; candidates [B_c x d] from H
+        F += 2.0 * B_r * (2 * d) * H + 2.0 * B_c * d * H
+        # bytes: activations read/written once, weights once, Z once (fp32 write + read)
+        Bts += 2 * (B_r + B_c) * d + 2 * (B_r + B_c) * H          # up: read x, write h
+        Bts += 2 * (2 * H * d + H * d)                              # up weights W_RR, W_CR, W_CC
+        Bts += 2 * 4 * B_r * H                                      # Z write + read
+        Bts += 2 * (B_r + B_c) * H + 2 * 2 * (B_r + B_c) * d        # down: read h, read residual, write o
+        Bts += 2 * (2 * d * H + d * H) + 2 * 4 * B_r * d
+        Bts += 2 * 2 * (B_r + B_c) * d                              # RMSNorm read + write
+        Bts += 4 * B_c                                              # cand2req reads
+    F += 2.0 * B_r * d + 2.0 * B_c * d                              # head
+    Bts += 2 * (B_r + B_c) * d + 4 * B_c
+    return F, Bts
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def candidate_gemm_roofline(st, reps=20):
+    """Times the IKBO candidate GEMM alone: the candidate halves of the stack's
+    GLM linears, launched through rocs_lcb_candidate on torch's current stream
+    and bracketed by events on that stream."""
+    import torch
+    from request_candidate_sharing_amd import rocs as R
+
+    cfg = st.cfg
+    B_r, B_c = st.B_r, st.B_c
+    d, H = cfg.d_r, cfg.hidden
+    g = torch.Generator(device="cuda").manual_seed(0)
+    bf = torch.bfloat16
+    shapes = [(d, H, False), (H, d, True)]  # (K, N, residual)
+    bufs = []
+    for K, N, res in shapes:
+        bufs.append(dict(
+            K=K, N=N, res=res,
+            x=torch.randn(B_c, K, generator=g, device="cuda").to(bf),
+            w=(torch.randn(N, K, generator=g, device="cuda") * K ** -0.5).to(bf),
+            z=torch.randn(B_r, N, generator=g, device="cuda"),
+            r=torch.randn(B_c, N, generator=g, device="cuda").to(bf) if res else None,
+            y=torch.empty(B_c, N, device="cuda", dtype=bf)))
+    s = R.cur_stream()
+
+    def launch(b):
+        R.rocs_lcb_candidate(st.batch, R.ROCS_BF16, b["x"], b["K"], b["K"], b["w"], None, b["N"],
+                             R.ROCS_ACT_NONE if b["res"] else R.ROCS_ACT_RELU, b["z"], b["N"], b["r"],
+                             b["N"] if b["res"] else 0, b["y"], b["N"], s)
+
+    for _ in range(3):
+        for b in bufs:
+            launch(b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for b in bufs:
+            launch(b)
+    e1.record()
+    torch.cuda.synchronize()
+    n = reps * len(bufs)
+    t = e0.elapsed_time(e1) / 1e3 / n
+    flops = np.mean([2.0 * B_c * b["N"] * b["K"] for b in bufs])
+    byts = np.mean([2.0 * B_c * b["K"] + 2.0 * B_c * b["N"] + 2.0 * b["N"] * b["K"] + 4.0 * B_r * b["N"] + 4.0 * B_c
+                    + (2.0 * B_c * b["N"] if b["res"] else 0.0) for b in bufs])
+    t_mfma, t_hbm = flops / PEAK_BF16, byts / PEAK_HBM
+    if t_hbm >= t_mfma:
+        rf = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        rf = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
+    rf["frac"] = rf["achieved"] / rf["peak"]
+    rf["traffic"] = None
+    rf["kernel"] = "gemm_bf16_kernel<128,128> (rocs_lcb_candidate: IKBO candidate GEMM + Z[m_i] gather epilogue)"
+    rf["avg_launch_us"] = t * 1e6
+    rf["alg_flops_per_launch"] = flops
+    rf["alg_bytes_per_launch"] = byts
+    rf["mfma_frac"] = flops / t / PEAK_BF16
+    return rf
+
+
+def cpu_baseline(inp, seconds):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    counts = inp["counts"]
+    done, n_req, t_total = 0, 0, 0.0
+    for b in range(len(counts)):
+        if counts[b] == 0:
+            continue
+        t0 = time.perf_counter()
+        oracle.oracle_forward(inp, requests=[b])
+        t_total += time.perf_counter() - t0
+        done += int(counts[b])
+        n_req += 1
+        if t_total >= seconds:
+            break
+    return {"value": done / t_total, "unit": "candidates/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 numpy oracle (dense masked model, materialized broadcast) on requests 0..{n_req - 1} "
+                      f"of the same batch: {done} candidates in {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-broadcast comparator")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--roofline-reps", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the ROCS stack on a single MI355X "
+              "(requests shard across GPUs with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    torch.cuda.set_device(0)
+    cfg = S.config(2)
+    inp = S.make_inputs(cfg)
+    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+    log(f"bench: {cfg.name()} B_r={B_r} B_c={B_c}")
+
+    shared = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+    t_sh, wall_sh = time_steps(shared.run, args.steps, args.warmup)
+    ms = t_sh / args.steps * 1e3
+    value = B_c * args.steps / t_sh
+    log(f"bench: shared {ms:.3f} ms/step, {value:.4g} candidates/s (wall {wall_sh:.3f} s)")
+    F, Bts = glm_mlp_work(cfg, B_r, B_c)
+    step_s = t_sh / args.steps
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) features, N(0,1/fan_in) weights)",
+        "config": {
+            "workload": "GLM MLP stack: B_r=256 requests, candidates/request ~U{64..512} (B_c=%d), d_R=d_C=512, "
+                        "3 GLM MLP blocks (hidden 1024 per group, ReLU) + residual + group-local RMSNorm, "
+                        "scalar GLM head; bf16 storage, fp32 accumulate" % B_c,
+            "B_r": B_r, "B_c": B_c, "global_batch": B_c, "seq_len": 0, "parallelism": "single GPU",
+        },
+        "mfma_util_pct": 100.0 * F / step_s / PEAK_BF16,
+        "hbm_util_pct": 100.0 * Bts / step_s / PEAK_HBM,
+        "alg_flops_per_step": F,
+        "alg_bytes_per_step": Bts,
+    }
+    if not args.no_dense:
+        dense = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+        t_de, _ = time_steps(dense.run, args.steps, args.warmup)
+        out["dense_broadcast"] = {"value": B_c * args.steps / t_de, "ms_per_step": t_de / args.steps * 1e3}
+        out["speedup_vs_dense_broadcast"] = t_de / t_sh
+        log(f"bench: dense broadcast {t_de / args.steps * 1e3:.3f} ms/step, speedup {t_de / t_sh:.3f}x")
+        del dense
+    out["roofline"] = candidate_gemm_roofline(shared, args.roofline_reps)
+    log(f"bench: candidate GEMM {out['roofline']['avg_launch_us']:.1f} us/launch, "
+        f"{out['roofline']['achieved']:.1f} {out['roofline']['unit']} ({out['roofline']['frac']:.3f} of peak)")
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        log(f"bench: cpu oracle {out['cpu_baseline']['value']:.4g} candidates/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,317 @@
+/*
+ * librocs -- C ABI of the ROCS (Request-Oriented Compute Sharing) shared
+ * forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * Citations name the web pages by title:
+ *   [R] "ROCS：面向请求的大规模推荐计算共享" (liuzhao09.github.io review):
+ *       §2.1 Generalized Layer Masking, §2.2 Deep Cross Attention,
+ *       §2.4 In-Kernel Broadcast Optimization, §4 summary.
+ *   [D] "Meta推出ROCS：推荐系统推理效率提升3倍，零质量损失" (longzhangge.com
+ *       PaperDaily digest), section on kernel-level optimisation (IKBO).
+ *
+ * The ragged batch ([R] §1 and §2.4): B_r requests, B_c candidates, and a map
+ * m (cand2req) with m[i] = the request of candidate i.  Request tensors stay
+ * at request-batch size B_r and candidate tensors at candidate-batch size
+ * B_c; every candidate-side kernel resolves m[i] itself, so no broadcast
+ * tensor is ever materialized ([R] §2.4) -- except in the explicitly
+ * requested dense-broadcast comparator mode of rocs_stack_forward.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument named as a tensor is DEVICE memory owned by the
+ *    caller.  The library never allocates device memory, never frees a
+ *    caller pointer and keeps no pointer after the call returns.  Scratch
+ *    memory is caller-provided ("workspace") and sized by the matching
+ *    *_workspace_size() call.  Host arrays are marked "host".
+ *  - Matrices are row-major.  ld_* arguments are leading dimensions (row
+ *    strides) in ELEMENTS of the tensor's dtype.  Weights are [out, in]
+ *    (row = one output channel), so both GEMM operands are contiguous along
+ *    the reduction axis.
+ *  - Alignment (the padding rule of [R] §2.4 and [D]): every tensor base
+ *    address must be 16-byte aligned and every ld must be a multiple of 16
+ *    bytes (8 bf16 or 4 fp32 elements); otherwise ROCS_ERR_ALIGN.  Widths
+ *    themselves may be any size; the stack executor pads its own buffers.
+ *  - dtype selects the element type of activations, weights, biases and
+ *    outputs: ROCS_F32, or ROCS_BF16 with fp32 accumulation.  Buffers named
+ *    z, logits and scale/eps are always fp32.
+ *  - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream) and return after enqueueing.  Host-side
+ *    argument validation runs before any HIP call, so invalid arguments
+ *    never touch the device.  A HIP launch error returns ROCS_ERR_HIP.
+ *  - Status codes are below; rocs_last_error() returns a thread-local
+ *    message for the last failing call.  No C++ exception crosses the ABI.
+ *  - Empty batches: B_c = 0 is a successful no-op for candidate outputs; a
+ *    request with zero candidates is legal.
+ *  - cand2req values must lie in [0, B_r).  Kernels never read outside the
+ *    request tensors: a candidate whose map entry is out of range gets NaN
+ *    outputs.  rocs_validate_batch() checks a batch explicitly.
+ *  - Results are deterministic: no atomics on any output path, and no
+ *    reduction order depends on B_r, B_c or the batch composition, so a
+ *    request's outputs are bit-identical whatever candidates accompany it.
+ */
+#ifndef ROCS_H_
+#define ROCS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROCS_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+enum rocs_status {
+  ROCS_OK = 0,
+  ROCS_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum */
+  ROCS_ERR_SHAPE = -2,       /* inconsistent dimensions (ld < width, ...) */
+  ROCS_ERR_DTYPE = -3,       /* dtype not supported by this call */
+  ROCS_ERR_ALIGN = -4,       /* base not 16-B aligned or ld*elem % 16 != 0 */
+  ROCS_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  ROCS_ERR_BATCH = -6,       /* offsets/cand2req inconsistent (rocs_validate_batch) */
+  ROCS_ERR_HIP = -7,         /* HIP launch or runtime error */
+  ROCS_ERR_UNSUPPORTED = -8  /* valid request outside the implemented envelope */
+};
+
+typedef enum rocs_dtype { ROCS_F32 = 0, ROCS_BF16 = 1 } rocs_dtype;
+typedef enum rocs_act { ROCS_ACT_NONE = 0, ROCS_ACT_RELU = 1 } rocs_act;
+typedef enum rocs_norm { ROCS_NORM_LAYER = 0, ROCS_NORM_RMS = 1 } rocs_norm;
+
+/* Ragged request/candidate batch ([R] §2.4: the index map m).
+ * cand2req (device, [num_candidates]) is authoritative.  offsets (device,
+ * [num_requests+1] prefix sums) may be given when candidates are stored
+ * contiguously per request (request b owns rows offsets[b]..offsets[b+1]-1);
+ * it lets attention tile queries per request without a sort.  NULL means
+ * arbitrary candidate order. */
+typedef struct rocs_batch {
+  int32_t num_requests;
+  int32_t num_candidates;
+  const int32_t* offsets;
+  const int32_t* cand2req;
+} rocs_batch;
+
+/* ------------------------------------------------------------------ GLM linear (LCB)
+ * [R] §2.1 masked-weight linear equation and two-group block matrix:
+ *   [Y_R; Y_C] = [[W_RR, 0], [W_CR, W_CC]] [X_R; X_C] + b
+ * executed in the decomposed form of [R] §2.4:
+ *   request batch   y_r = act(x_r W_RR^T + b_r) + res_r,   z = x_r W_CR^T (fp32)
+ *   candidate batch y_c[i] = act(x_c[i] W_CC^T + z[m_i] + b_c) + res_c[i]
+ * The candidate GEMM adds z[m_i] in its epilogue (in registers; no
+ * broadcast tensor, no intermediate written).  The request half is one GEMM
+ * over the stacked weight [W_RR; W_CR].
+ *
+ * Shapes: x_r [B_r, d_in_r] (ld_xr), x_c [B_c, d_in_c] (ld_xc),
+ * w_rr [d_out_r, d_in_r], w_cr [d_out_c, d_in_r], w_cc [d_out_c, d_in_c]
+ * (dense, ld = in width), b_r [d_out_r], b_c [d_out_c] (nullable = 0),
+ * res_r [B_r, d_out_r] (ld_resr, nullable), res_c [B_c, d_out_c] (ld_resc,
+ * nullable), y_r [B_r, d_out_r] (ld_yr), y_c [B_c, d_out_c] (ld_yc),
+ * z [B_r, d_out_c] fp32 (ld_z; caller scratch, overwritten).
+ * d_out_r may be 0 (then w_rr, b_r, res_r, y_r are ignored).  Weight base
+ * addresses must be 16-B aligned and in widths multiples of 16 bytes.
+ * Outputs may not alias inputs. */
+int rocs_lcb_request(rocs_dtype dtype, int32_t B_r, const void* x_r, int64_t ld_xr, int32_t d_in_r,
+                     const void* w_rr, const void* w_cr, const void* b_r, int32_t d_out_r, int32_t d_out_c,
+                     rocs_act act, const void* res_r, int64_t ld_resr, void* y_r, int64_t ld_yr, float* z,
+                     int64_t ld_z, void* stream);
+
+int rocs_lcb_candidate(const rocs_batch* batch, rocs_dtype dtype, const void* x_c, int64_t ld_xc,
+                       int32_t d_in_c, const void* w_cc, const void* b_c, int32_t d_out_c, rocs_act act,
+                       const float* z, int64_t ld_z, const void* res_c, int64_t ld_resc, void* y_c,
+                       int64_t ld_yc, void* stream);
+
+int rocs_lcb_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r, int64_t ld_xr, int32_t d_in_r,
+                     const void* x_c, int64_t ld_xc, int32_t d_in_c, const void* w_rr, const void* w_cr,
+                     const void* w_cc, const void* b_r, const void* b_c, int32_t d_out_r, int32_t d_out_c,
+                     rocs_act act, const void* res_r, int64_t ld_resr, const void* res_c, int64_t ld_resc,
+                     void* y_r, int64_t ld_yr, void* y_c, int64_t ld_yc, float* z, int64_t ld_z, void* stream);
+
+/* ------------------------------------------------------------------ scalar head
+ * The GLM linear of [R] §2.1 with d_out_r = 0 and d_out_c = 1 (a candidate
+ * score): z[b] = w_cr . x_r[b];  logits[i] = w_cc . x_c[i] + z[m_i] + bias.
+ * x_r [B_r, d_r] (ld_xr), x_c [B_c, d_c] (ld_xc), w_cr [d_r], w_cc [d_c],
+ * z [B_r] fp32 scratch, logits [B_c] fp32. */
+int rocs_head_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r, int64_t ld_xr, int32_t d_r,
+                      const void* x_c, int64_t ld_xc, int32_t d_c, const void* w_cr, const void* w_cc,
+                      float bias, float* z, float* logits, void* stream);
+
+/* ------------------------------------------------------------------ group-local norm
+ * [R] §2.1, Figure 2(b): statistics per group, never across groups.
+ *   y = act(norm(x + res) * gamma + beta)
+ * LAYER: (v - mean) / sqrt(biased var + eps); RMS: v / sqrt(mean(v^2) + eps).
+ * Statistics in fp32 over each row of one group's slice.  Request rows
+ * x_r [rows_r, width_r], candidate rows x_c [rows_c, width_c]; res_* share
+ * the ld of x_* and are nullable; gamma/beta [width] nullable (1 / 0).
+ * In place (y == x) is allowed. */
+int rocs_group_norm(rocs_dtype dtype, rocs_norm kind, float eps, int32_t rows_r, int32_t width_r, int32_t rows_c,
+                    int32_t width_c, const void* x_r, int64_t ld_xr, const void* x_c, int64_t ld_xc,
+                    const void* res_r, const void* res_c, const void* gamma_r, const void* beta_r,
+                    const void* gamma_c, const void* beta_c, rocs_act act_after, void* y_r, int64_t ld_yr,
+                    void* y_c, int64_t ld_yc, void* stream);
+
+/* ------------------------------------------------------------------ masked FM
+ * [R] §2.1 masked-FM equation, Figure 2(c): with request tokens
+ * X_R[b] [n_r, dim] and candidate tokens X_C[i] [n_c, dim],
+ *   f_r[b] = vec(X_R[b] X_R[b]^T)                   (n_r*n_r values)
+ *   f_c[i] = vec(X_C[i] [X_R[m_i]; X_C[i]]^T)         (n_c*(n_r+n_c) values)
+ * flattened token-major (row a, then columns; candidate columns list the
+ * request tokens first).  The structurally zero request x candidate block
+ * is not stored.  x_r [B_r, n_r*dim], x_c [B_c, n_c*dim] contiguous rows;
+ * f_r (ld_fr), f_c (ld_fc).  bf16 only; dim % 32 == 0, n_r <= 64,
+ * n_c <= 64. */
+int rocs_fm_masked(const rocs_batch* batch, rocs_dtype dtype, int32_t n_r, int32_t n_c, int32_t dim,
+                   const void* x_r, int64_t ld_xr, const void* x_c, int64_t ld_xc, void* f_r, int64_t ld_fr,
+                   void* f_c, int64_t ld_fc, void* stream);
+
+/* ------------------------------------------------------------------ token-axis LCB
+ * The GLM linear of [R] §2.1 applied along the token axis (the LCB
+ * compression of Figure 1(d)):  T_R[b] = W_RR X_R[b];
+ * T_C[i] = W_CC X_C[i] + Z[m_i] with Z[b] = W_CR X_R[b] computed once per
+ * request ([R] §2.4).  w_rr [t_r, n_r], w_cr [t_c, n_r], w_cc [t_c, n_c]
+ * (dense, same dtype), x_* as in rocs_fm_masked, outputs flattened
+ * token-major: y_r [B_r, t_r*dim] (ld_yr), y_c [B_c, t_c*dim] (ld_yc),
+ * z [B_r, t_c*dim] fp32 scratch.  bf16 only; dim % 64 == 0, n_r, n_c <= 64,
+ * t_r, t_c <= 256. */
+int rocs_token_lcb(const rocs_batch* batch, rocs_dtype dtype, int32_t n_r, int32_t n_c, int32_t dim, int32_t t_r,
+                   int32_t t_c, const void* x_r, int64_t ld_xr, const void* x_c, int64_t ld_xc, const void* w_rr,
+                   const void* w_cr, const void* w_cc, void* y_r, int64_t ld_yr, void* y_c, int64_t ld_yc,
+                   float* z, void* stream);
+
+/* ------------------------------------------------------------------ DCA
+ * [R] §2.2: a request-only sequence encoder S_k = Enc_k(S_{k-1}) and per
+ * interaction depth the shared projections K = S W_K, V = S W_V for the
+ * request and candidate query groups, computed once per request.
+ * Encoder layer (post-LN, ReLU FFN, no mask):
+ *   S' = LN(S + MHA(S)),  S'' = LN(S' + W_2 ReLU(W_1 S' + b_1) + b_2),
+ * MHA with a fused in-projection [3d, d] (q, k, v row blocks) + bias and an
+ * output projection [d, d] + bias; heads are contiguous head_dim slices. */
+typedef struct rocs_enc_layer {
+  const void* w_qkv; const void* b_qkv; /* [3d, d], [3d] (bias nullable) */
+  const void* w_o;   const void* b_o;   /* [d, d],  [d] */
+  const void* ln1_g; const void* ln1_b; /* [d] nullable (1 / 0) */
+  const void* w_1;   const void* b_1;   /* [ffn, d], [ffn] */
+  const void* w_2;   const void* b_2;   /* [d, ffn], [d] */
+  const void* ln2_g; const void* ln2_b; /* [d] nullable */
+} rocs_enc_layer;
+
+typedef struct rocs_kv_w {
+  const void* wk_r; const void* wv_r; const void* wk_c; const void* wv_c; /* each [d, d], no bias */
+} rocs_kv_w;
+
+/* Encodes the sequences and writes every depth's keys/values.
+ * seq [B_r, L, d] contiguous.  kv (output) is [n_depths][B_r*L][4*d]: row
+ * (b*L + l) of depth j holds [K_R | V_R | K_C | V_C] of token l of request b.
+ * depth_src (host, [n_depths]) picks the encoder output each depth reads
+ * (0 = raw sequence, k = after layer k).  enc (host, [n_enc]), kvw (host,
+ * [n_depths]).  bf16 only; head_dim == 64; d = n_heads*64; ffn % 8 == 0.
+ * workspace >= rocs_dca_encode_kv_workspace_size(B_r, L, d, ffn, n_enc). */
+size_t rocs_dca_encode_kv_workspace_size(int32_t B_r, int32_t L, int32_t d, int32_t ffn, int32_t n_enc);
+int rocs_dca_encode_kv(rocs_dtype dtype, int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t ffn,
+                       const void* seq, int32_t n_enc, const rocs_enc_layer* enc, int32_t n_depths,
+                       const int32_t* depth_src, const rocs_kv_w* kvw, void* kv, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/* Grouped cross-attention ([R] §2.2, IKBO-DCA of [R] §2.4): per head h,
+ *   a_r[b]_h = softmax(q_r[b]_h K_R[b]_h^T * scale) V_R[b]_h
+ *   a_c[i]_h = softmax(q_c[i]_h K_C[m_i]_h^T * scale) V_C[m_i]_h
+ * with no mask.  Keys/values stay at request-batch size: k_* / v_* point at
+ * [B_r][L] rows of row stride ld_kv elements (request b's token l is row
+ * b*L + l); head h uses columns [h*64, h*64+64).  All queries of one
+ * request share each staged key/value tile.  q_r [B_r, H*64] (ld_qr),
+ * q_c [B_c, H*64] (ld_qc); outputs a_r (ld_ar), a_c (ld_ac).  q_r/a_r
+ * nullable (skip the request group).  bf16 only, head_dim == 64,
+ * scale <= 0 selects 1/sqrt(head_dim).  workspace >=
+ * rocs_dca_cross_attn_workspace_size(B_r, B_c) (per-request query tiles
+ * and, when batch->offsets is NULL, a device counting sort of cand2req). */
+size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c);
+int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim, int32_t L,
+                        const void* q_r, int64_t ld_qr, const void* q_c, int64_t ld_qc, const void* k_r,
+                        const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv, float scale, void* a_r,
+                        int64_t ld_ar, void* a_c, int64_t ld_ac, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ explicit broadcast (comparator)
+ * dst row i = src row m_i, copied byte for byte (the materialized broadcast
+ * of [R] §2.4, Figure 3(a); used only by the dense-broadcast comparator).
+ * row_bytes % 16 == 0; strides in bytes, multiples of 16. */
+int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* src, int64_t src_stride,
+                        void* dst, int64_t dst_stride, void* stream);
+
+/* ------------------------------------------------------------------ stack executor
+ * Runs a ROCSified layer stack ([R] §2.1 composition closure) on one
+ * stream.  Activations live in "slots": slot 0 is the caller's input
+ * (io->x_r / io->x_c), slot 1 the caller's output (io->y_r / io->y_c), and
+ * slots >= 2 are carved from the workspace with 16-byte-padded rows.  Each
+ * slot has a request part [B_r, width_r] and a candidate part
+ * [B_c, width_c].  Layers read and write column ranges of slots, so a
+ * concatenation is two layers writing adjacent columns of one slot. */
+typedef enum rocs_exec_mode {
+  ROCS_EXEC_SHARED = 0,         /* request work at B_r size, map resolved in-kernel */
+  ROCS_EXEC_DENSE_BROADCAST = 1 /* comparator: request contributions and K/V copied to B_c rows first */
+} rocs_exec_mode;
+
+typedef enum rocs_op_kind {
+  ROCS_OP_LINEAR = 1,    /* rocs_lcb_forward                                      */
+  ROCS_OP_NORM = 2,      /* rocs_group_norm                                        */
+  ROCS_OP_FM = 3,        /* rocs_fm_masked, src holds tokens [n_r*dim | n_c*dim]   */
+  ROCS_OP_TOKEN_LCB = 4, /* rocs_token_lcb (w_rr, w_cr, w_cc are the token maps)   */
+  ROCS_OP_XATTN = 5,     /* rocs_dca_cross_attn at K/V depth `depth`; src = queries */
+  ROCS_OP_HEAD = 6       /* rocs_head_forward into io->logits; b_c[0] = bias        */
+} rocs_op_kind;
+
+typedef struct rocs_layer {
+  int32_t kind;                    /* rocs_op_kind */
+  int32_t src, src_col_r, src_col_c; /* input slot and per-group column offsets */
+  int32_t dst, dst_col_r, dst_col_c; /* output slot and per-group column offsets */
+  int32_t res, res_col_r, res_col_c; /* residual slot (-1 = none) */
+  int32_t d_in_r, d_in_c, d_out_r, d_out_c; /* per-group widths */
+  int32_t act;                     /* rocs_act: LINEAR before the residual, NORM after */
+  int32_t norm;                    /* rocs_norm (NORM) */
+  float eps;                       /* NORM */
+  int32_t depth;                   /* XATTN: K/V depth index */
+  int32_t n_r, n_c, dim;           /* FM / TOKEN_LCB token counts and token dim */
+  const void* w_rr; const void* w_cr; const void* w_cc;
+  const void* b_r; const void* b_c;
+  const void* gamma_r; const void* beta_r; const void* gamma_c; const void* beta_c;
+} rocs_layer;
+
+typedef struct rocs_slot { int32_t width_r, width_c; } rocs_slot;
+
+typedef struct rocs_dca_desc {
+  int32_t L, d, n_heads, ffn;
+  int32_t n_enc; const rocs_enc_layer* enc;   /* host [n_enc] */
+  int32_t n_depths; const int32_t* depth_src; /* host [n_depths] */
+  const rocs_kv_w* kvw;                       /* host [n_depths] */
+} rocs_dca_desc;
+
+typedef struct rocs_stack_desc {
+  rocs_dtype dtype;
+  rocs_exec_mode mode;
+  int32_t n_slots; const rocs_slot* slots;   /* host [n_slots], n_slots >= 2 */
+  int32_t n_layers; const rocs_layer* layers; /* host [n_layers] */
+  const rocs_dca_desc* dca;                  /* NULL when no layer is XATTN */
+} rocs_stack_desc;
+
+typedef struct rocs_stack_io {
+  const void* x_r; int64_t ld_xr; const void* x_c; int64_t ld_xc; /* slot 0 */
+  void* y_r; int64_t ld_yr; void* y_c; int64_t ld_yc;             /* slot 1 (nullable if unused) */
+  const void* seq;                                                /* DCA sequences [B_r, L, d] */
+  float* logits;                                                  /* HEAD output [B_c] */
+} rocs_stack_io;
+
+size_t rocs_stack_workspace_size(const rocs_stack_desc* desc, int32_t B_r, int32_t B_c);
+int rocs_stack_forward(const rocs_stack_desc* desc, const rocs_batch* batch, const rocs_stack_io* io,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ utilities */
+/* Checks offsets/cand2req on the device (synchronizes `stream`): cand2req in
+ * range, and when offsets is given, offsets[0] == 0, offsets[B_r] == B_c,
+ * nondecreasing, and cand2req[i] == b for every i in request b's range.
+ * Returns ROCS_OK or ROCS_ERR_BATCH. */
+int rocs_validate_batch(const rocs_batch* batch, void* stream);
+const char* rocs_status_str(int status);
+const char* rocs_last_error(void);
+int rocs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROCS_H_ */

@@ -1,0 +1,159 @@
+// Internal kernel interfaces of librocs (gfx950 only).  Host validation lives
+// in rocs_api.cpp; everything here assumes arguments were already checked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rocs {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum DType { F32 = 0, BF16 = 1 };
+
+// C[M,N] = A[M,K] . W[N,K]^T followed by the GLM epilogue.
+// Columns [0, n_split) go to out0 through the full epilogue
+//   v = acc + z[zrow(m)][n] + bias[n];  v = act(v);  v += res[m][n]
+// with zrow(m) = zmap ? zmap[m] : m (the in-kernel broadcast of the
+// request contribution); columns [n_split, N) go raw to out1 (fp32).
+// The weight operand may be split into up to four row segments (e.g. the
+// stacked [W_RR; W_CR] of the request half, or [Wk_R; Wv_R; Wk_C; Wv_C]),
+// segment s covering rows [seg_end[s-1], seg_end[s]).
+struct GemmArgs {
+  int M, N, K;
+  const void* A;
+  int64_t lda;
+  int nseg;
+  const void* W[4];
+  int seg_end[4];
+  int64_t ldw;
+  int n_split;
+  void* out0;
+  int64_t ld0;
+  int out0_f32;  // 1: out0 is fp32 even for bf16 compute
+  float* out1;
+  int64_t ld1;
+  const float* z;
+  int64_t ldz;
+  const int32_t* zmap;
+  int zrows;
+  const void* bias;
+  int act;
+  const void* res;
+  int64_t ldres;
+};
+
+hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
+
+// y = act(norm(x + res) * gamma + beta) on rows of width w (one launch per group).
+struct NormArgs {
+  int rows, width;
+  const void* x;
+  int64_t ldx;
+  const void* res;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  int64_t ldy;
+  int kind;  // 0 layer, 1 rms
+  float eps;
+  int act;
+  int64_t ldres;  // 0: same as ldx
+};
+hipError_t launch_norm(DType dt, const NormArgs& a, hipStream_t s);
+
+// dot rows: out[i] = w . x[i] (+ z[zmap[i]]) (+ bias)
+struct DotArgs {
+  int rows, width;
+  const void* x;
+  int64_t ldx;
+  const void* w;
+  const float* z;
+  const int32_t* zmap;
+  int zrows;
+  float bias;
+  const void* bias_dev;  // optional device scalar (dtype of x), added after bias
+  float* out;
+};
+hipError_t launch_rowdot(DType dt, const DotArgs& a, hipStream_t s);
+
+// dst row r = src row (map[r / inner] * inner + r % inner), rows = map entries * inner.
+hipError_t launch_broadcast_rows(int rows, const int32_t* map, int map_rows, int64_t row_bytes, const void* src,
+                                 int64_t src_stride, void* dst, int64_t dst_stride, hipStream_t s, int inner = 1);
+
+// Grouped attention, bf16, head_dim 64.  Query rows are grouped; group g
+// attends keys/values rows [g*L, g*L + L) (row stride ldkv) of its K/V.
+// Query tiles come from a tile table (see launch_attn_plan) or, for uniform
+// groups (q_rows_per_group > 0), are implicit.
+struct AttnArgs {
+  int n_heads;
+  int L;
+  const bf16* q;
+  int64_t ldq;
+  const bf16* k;
+  const bf16* v;
+  int64_t ldkv;
+  int64_t kv_group_stride;  // elements between groups (normally L*ldkv)
+  bf16* o;
+  int64_t ldo;
+  float scale_log2;  // scale * log2(e)
+  // grouping
+  int n_groups;
+  int q_rows_per_group;      // > 0: uniform groups, row r belongs to group r / q_rows_per_group
+  const int32_t* tile_info;  // per tile: group, row_begin, row_end (3 ints), from the plan
+  const int32_t* n_tiles_dev;
+  const int32_t* perm;  // optional row permutation: logical row r is physical row perm[r]
+  int max_tiles;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+int attn_tile_rows();
+
+// Builds per-request query tiles (and, without offsets, a counting sort of
+// cand2req into a permutation).  ws layout is returned through the pointers.
+size_t attn_plan_ws_bytes(int B_r, int B_c);
+hipError_t launch_attn_plan(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, void* ws,
+                            int32_t** tile_info, int32_t** n_tiles, int32_t** perm, int* max_tiles, hipStream_t s);
+
+struct FmArgs {
+  int B_r, B_c, n_r, n_c, dim;
+  const bf16* x_r;
+  int64_t ldxr;
+  const bf16* x_c;
+  int64_t ldxc;
+  const int32_t* map;  // cand2req (NULL: candidate i reads request row i)
+  int map_rows;
+  bf16* f_r;
+  int64_t ldfr;
+  bf16* f_c;
+  int64_t ldfc;
+};
+hipError_t launch_fm(const FmArgs& a, hipStream_t s);
+
+struct TokLcbArgs {
+  int B_r, B_c, n_r, n_c, dim, t_r, t_c;
+  const bf16* x_r;
+  int64_t ldxr;
+  const bf16* x_c;
+  int64_t ldxc;
+  const bf16* w_rr;
+  const bf16* w_cr;
+  const bf16* w_cc;
+  bf16* y_r;
+  int64_t ldyr;
+  bf16* y_c;
+  int64_t ldyc;
+  float* z;
+  const int32_t* map;
+  int map_rows;
+};
+hipError_t launch_token_lcb_request(const TokLcbArgs& a, hipStream_t s);
+hipError_t launch_token_lcb_candidate(const TokLcbArgs& a, hipStream_t s);
+
+hipError_t launch_validate_batch(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, int32_t* flag,
+                                 hipStream_t s);
+
+}  // namespace rocs

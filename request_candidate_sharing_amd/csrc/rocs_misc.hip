@@ -1,0 +1,230 @@
+// Group-local norms, the scalar score head, the explicit broadcast used by
+// the dense-broadcast comparator, and batch validation.
+#include "rocs_device.h"
+
+namespace rocs {
+
+namespace {
+
+// ----------------------------------------------------------------- group-local norm
+// [R] §2.1, Figure 2(b): statistics inside one group's slice of a row.  One
+// wave per row; the row (x + res) stays in registers between the statistics
+// and the normalisation, so each element is read once and written once.
+// LayerNorm: two-pass mean / biased variance in fp32; RMSNorm: mean square.
+template <typename T, int CH>
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
+  const T* r = a.res ? reinterpret_cast<const T*>(a.res) + int64_t(row) * (a.ldres ? a.ldres : a.ldx) : nullptr;
+  float v[CH][VEC];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e0 = (c * 64 + lane) * VEC;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) v[c][j] = 0.f;
+    if (e0 + VEC <= a.width) {
+      const uint4 u = *reinterpret_cast<const uint4*>(x + e0);
+      const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) v[c][j] = to_f(t[j]);
+      if (r) {
+        const uint4 ur = *reinterpret_cast<const uint4*>(r + e0);
+        const T* tr = reinterpret_cast<const T*>(&ur);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[c][j] += to_f(tr[j]);
+      }
+    } else {
+      for (int j = 0; j < VEC; ++j)
+        if (e0 + j < a.width) v[c][j] = to_f(x[e0 + j]) + (r ? to_f(r[e0 + j]) : 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s += (a.kind == 0) ? v[c][j] : v[c][j] * v[c][j];
+  }
+  const float inv_w = 1.0f / float(a.width);
+  float mean = 0.f, scale;
+  if (a.kind == 0) {
+    mean = wave_sum(s) * inv_w;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e0 = (c * 64 + lane) * VEC;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        if (e0 + j < a.width) {
+          const float d = v[c][j] - mean;
+          q += d * d;
+        }
+    }
+    scale = 1.0f / sqrtf(wave_sum(q) * inv_w + a.eps);
+  } else {
+    scale = 1.0f / sqrtf(wave_sum(s) * inv_w + a.eps);
+  }
+  const T* g = reinterpret_cast<const T*>(a.gamma);
+  const T* b = reinterpret_cast<const T*>(a.beta);
+  T* y = reinterpret_cast<T*>(a.y) + int64_t(row) * a.ldy;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e0 = (c * 64 + lane) * VEC;
+    if (e0 >= a.width) continue;
+    T out[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const int e = min(e0 + j, a.width - 1);
+      float t = (v[c][j] - mean) * scale;
+      if (g) t *= to_f(g[e]);
+      if (b) t += to_f(b[e]);
+      if (a.act == 1) t = fmaxf(t, 0.f);
+      out[j] = from_f<T>(t);
+    }
+    if (e0 + VEC <= a.width) {
+      *reinterpret_cast<uint4*>(y + e0) = *reinterpret_cast<const uint4*>(out);
+    } else {
+      for (int j = 0; j < VEC; ++j)
+        if (e0 + j < a.width) y[e0 + j] = out[j];
+    }
+  }
+}
+
+template <typename T>
+hipError_t norm_dispatch(const NormArgs& a, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int per = 64 * VEC;
+  const int ch = (a.width + per - 1) / per;
+  const dim3 grid((a.rows + 3) / 4), block(256);
+  if (ch <= 1)
+    hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, s, a);
+  else if (ch <= 2)
+    hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, s, a);
+  else if (ch <= 4)
+    hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a);
+  else if (ch <= 8)
+    hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a);
+  else if (ch <= 16)
+    hipLaunchKernelGGL((norm_kernel<T, 16>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- row dot (score head)
+// out[i] = w . x[i] + z[map[i]] + bias, one wave per row, fixed reduction order.
+template <typename T>
+__global__ __launch_bounds__(256) void rowdot_kernel(DotArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
+  const T* w = reinterpret_cast<const T*>(a.w);
+  float s = 0.f;
+  for (int e0 = lane * VEC; e0 < a.width; e0 += 64 * VEC) {
+    if (e0 + VEC <= a.width) {
+      const uint4 ux = *reinterpret_cast<const uint4*>(x + e0);
+      const uint4 uw = *reinterpret_cast<const uint4*>(w + e0);
+      const T* tx = reinterpret_cast<const T*>(&ux);
+      const T* tw = reinterpret_cast<const T*>(&uw);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) s = fmaf(to_f(tx[j]), to_f(tw[j]), s);
+    } else {
+      for (int j = 0; j < VEC && e0 + j < a.width; ++j) s = fmaf(to_f(x[e0 + j]), to_f(w[e0 + j]), s);
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    if (a.z) {
+      const int m = a.zmap ? a.zmap[row] : row;
+      s = ((unsigned)m < (unsigned)a.zrows) ? s + a.z[m] : nan_f();
+    }
+    s += a.bias;
+    if (a.bias_dev) s += to_f(reinterpret_cast<const T*>(a.bias_dev)[0]);
+    a.out[row] = s;
+  }
+}
+
+// ----------------------------------------------------------------- explicit broadcast
+// dst[i] = src[map[i]] byte for byte; 16 bytes per thread.
+__global__ __launch_bounds__(256) void bcast_kernel(int64_t rows, const int32_t* map, int map_rows, int64_t chunks,
+                                                     const uint4* src, int64_t src_stride, uint4* dst,
+                                                     int64_t dst_stride, int inner) {
+  const int64_t total = rows * chunks;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total; e += int64_t(gridDim.x) * 256) {
+    const int64_t r = e / chunks, c = e - r * chunks;
+    const int64_t i = r / inner, l = r - i * inner;
+    const int m = map ? map[i] : int(i);
+    uint4 v = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    if ((unsigned)m < (unsigned)map_rows) v = src[(int64_t(m) * inner + l) * src_stride + c];
+    dst[r * dst_stride + c] = v;
+  }
+}
+
+// ----------------------------------------------------------------- batch validation
+__device__ int g_batch_flag;
+
+__global__ void clear_flag_kernel() { g_batch_flag = 0; }
+
+__global__ __launch_bounds__(256) void validate_kernel(int B_r, int B_c, const int32_t* offsets,
+                                                        const int32_t* cand2req) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < B_c) {
+    const int m = cand2req[i];
+    bool bad = (unsigned)m >= (unsigned)B_r;
+    if (!bad && offsets) bad = !(offsets[m] <= i && i < offsets[m + 1]);
+    if (bad) atomicOr(&g_batch_flag, 1);
+  }
+  if (offsets && i <= B_r) {
+    bool bad = false;
+    if (i == 0) bad = offsets[0] != 0;
+    if (i == B_r) bad = bad || offsets[B_r] != B_c;
+    if (i < B_r) bad = bad || offsets[i] > offsets[i + 1];
+    if (bad) atomicOr(&g_batch_flag, 2);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_norm(DType dt, const NormArgs& a, hipStream_t s) {
+  if (a.rows <= 0 || a.width <= 0) return hipSuccess;
+  return dt == F32 ? norm_dispatch<float>(a, s) : norm_dispatch<bf16>(a, s);
+}
+
+hipError_t launch_rowdot(DType dt, const DotArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const dim3 grid((a.rows + 3) / 4), block(256);
+  if (dt == F32)
+    hipLaunchKernelGGL(rowdot_kernel<float>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<bf16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_broadcast_rows(int rows, const int32_t* map, int map_rows, int64_t row_bytes, const void* src,
+                                 int64_t src_stride, void* dst, int64_t dst_stride, hipStream_t s, int inner) {
+  if (rows <= 0 || row_bytes <= 0 || inner <= 0) return hipSuccess;
+  const int64_t chunks = row_bytes / 16;
+  const int64_t all_rows = int64_t(rows) * inner;
+  const int64_t total = all_rows * chunks;
+  const int64_t want = (total + 255) / 256;
+  const int grid = int(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(bcast_kernel, dim3(grid), dim3(256), 0, s, all_rows, map, map_rows, chunks,
+                     reinterpret_cast<const uint4*>(src), src_stride / 16, reinterpret_cast<uint4*>(dst),
+                     dst_stride / 16, inner);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_batch(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, int32_t* flag,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, s);
+  const int n = (B_c > B_r + 1 ? B_c : B_r + 1);
+  hipLaunchKernelGGL(validate_kernel, dim3((n + 255) / 256), dim3(256), 0, s, B_r, B_c, offsets, cand2req);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbolAsync(flag, HIP_SYMBOL(g_batch_flag), sizeof(int32_t), 0, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(s);
+}
+
+}  // namespace rocs

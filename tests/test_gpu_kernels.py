@@ -1,0 +1,386 @@
+"""Per-call GPU parity: every librocs entry point against the CPU oracle.
+
+Inputs are seeded and synthetic; sizes span several tiles with ragged tails,
+empty requests and padded leading dimensions.  Floating-point parity uses
+max|gpu - oracle| / max|oracle| (fp32 <= 1e-5, bf16 <= 2e-2); gathers and
+small-integer problems are compared bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import rocs_synth as S
+from oracle import ops
+from gpu_util import TOL_BF16, TOL_F32, dev, rand, rel_err, to_np, tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _R():
+    from request_candidate_sharing_amd import rocs as R
+
+    return R
+
+
+def padded(rows, width, ld, dtype):
+    """[rows, width] view with leading dimension ld; returns (storage, view)."""
+    st = torch.full((max(rows, 1), ld), float("nan"), dtype=dtype, device="cuda")
+    return st, st[:rows, :width]
+
+
+def put(a, ld, dtype):
+    a = np.asarray(a, dtype=np.float32)
+    st, v = padded(a.shape[0], a.shape[1], ld, dtype)
+    if a.shape[0]:
+        v.copy_(torch.as_tensor(a, device="cuda").to(dtype))
+    return st, v
+
+
+def lcb_case(counts, d_in_r, d_in_c, d_out_r, d_out_c, dt, act, seed, bias=True, res=True, pad=16, ints=False,
+             x_c_override=None):
+    R = _R()
+    rng = np.random.default_rng(seed)
+    bf = dt == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    rdt = R.ROCS_BF16 if bf else R.ROCS_F32
+    bt = S.make_batch(counts)
+    B, Bc = len(counts), int(np.sum(counts))
+    if ints:
+        # request-side draws first, so they do not depend on the candidate count
+        x_r = rng.integers(-2, 3, (B, d_in_r)).astype(np.float32)
+        W = rng.integers(-1, 2, (d_out_r + d_out_c, d_in_r + d_in_c)).astype(np.float32)
+        b = rng.integers(-3, 4, d_out_r + d_out_c).astype(np.float32)
+        r_r = rng.integers(-3, 4, (B, d_out_r)).astype(np.float32)
+        x_c = rng.integers(-2, 3, (Bc, d_in_c)).astype(np.float32)
+        r_c = rng.integers(-3, 4, (Bc, d_out_c)).astype(np.float32)
+    else:
+        x_r = rand(rng, (B, d_in_r), bf)
+        W = rand(rng, (d_out_r + d_out_c, d_in_r + d_in_c), bf, (d_in_r + d_in_c) ** -0.5)
+        b = rand(rng, d_out_r + d_out_c, bf, 0.5)
+        r_r = rand(rng, (B, d_out_r), bf)
+        x_c = rand(rng, (Bc, d_in_c), bf)
+        r_c = rand(rng, (Bc, d_out_c), bf)
+    if x_c_override is not None:
+        x_c = x_c_override
+    if not bias:
+        b = np.zeros_like(b)
+    esz = 8 if bf else 4
+    ld = lambda w: ((w + pad + esz - 1) // esz) * esz
+    _, xr_t = put(x_r, ld(d_in_r), tdt)
+    _, xc_t = put(x_c, ld(d_in_c), tdt)
+    w_rr = dev(W[:d_out_r, :d_in_r], tdt)
+    w_cr = dev(W[d_out_r:, :d_in_r], tdt)
+    w_cc = dev(W[d_out_r:, d_in_r:], tdt)
+    b_r = dev(b[:d_out_r], tdt) if bias else None
+    b_c = dev(b[d_out_r:], tdt) if bias else None
+    rr_t = put(r_r, ld(d_out_r), tdt)[1] if res else None
+    rc_t = put(r_c, ld(d_out_c), tdt)[1] if res else None
+    _, yr_t = padded(B, d_out_r, ld(d_out_r), tdt)
+    _, yc_t = padded(Bc, d_out_c, ld(d_out_c), tdt)
+    zst, z_t = padded(B, d_out_c, ((d_out_c + 3) // 4) * 4 + 4, torch.float32)
+    off = torch.as_tensor(bt["offsets"], device="cuda")
+    c2r = torch.as_tensor(bt["cand2req"], device="cuda")
+    batch = R.batch(B, Bc, off, c2r)
+    R.rocs_lcb_forward(batch, rdt, xr_t, xr_t.stride(0), d_in_r, xc_t, xc_t.stride(0), d_in_c, w_rr, w_cr, w_cc, b_r,
+                       b_c, d_out_r, d_out_c, act, rr_t, rr_t.stride(0) if res else 0, rc_t,
+                       rc_t.stride(0) if res else 0, yr_t, yr_t.stride(0), yc_t, yc_t.stride(0), z_t, z_t.stride(0),
+                       R.cur_stream())
+    torch.cuda.synchronize()
+    # oracle: dense masked layer on the broadcast state (+ a zero candidate for request outputs)
+    m = bt["cand2req"]
+    dense_c = np.concatenate([x_r[m], x_c], 1)
+    dense_r = np.concatenate([x_r, np.zeros((B, d_in_c), np.float32)], 1)
+    yc = ops.glm_linear(dense_c, W, b, d_in_r, d_out_r)[:, d_out_r:]
+    yr = ops.glm_linear(dense_r, W, b, d_in_r, d_out_r)[:, :d_out_r]
+    if act == R.ROCS_ACT_RELU:
+        yc, yr = ops.relu(yc), ops.relu(yr)
+    if res:
+        yc, yr = yc + r_c, yr + r_r
+    zref = x_r.astype(np.float64) @ W[d_out_r:, :d_in_r].astype(np.float64).T
+    return dict(y_r=to_np(yr_t), y_c=to_np(yc_t), z=to_np(z_t), ref_r=yr, ref_c=yc, ref_z=zref, c2r=m)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize(
+    "counts,dims",
+    [
+        ([5, 0, 17, 1, 130, 2], (40, 24, 24, 56)),
+        ([300, 0, 77, 260, 1, 129], (136, 72, 200, 200)),
+        ([700, 600], (64, 520, 48, 1000)),
+        ([3, 4], (8, 8, 0, 16)),
+    ],
+)
+def test_lcb_forward_parity(dt, counts, dims):
+    R = _R()
+    out = lcb_case(counts, *dims, dt, R.ROCS_ACT_RELU, seed=sum(dims))
+    t = tol(dt)
+    assert rel_err(out["y_c"], out["ref_c"]) <= t
+    if dims[2] > 0:
+        assert rel_err(out["y_r"], out["ref_r"]) <= t
+    assert rel_err(out["z"], out["ref_z"]) <= (TOL_F32 if dt == "f32" else 1e-5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_lcb_small_integers_bit_exact(dt):
+    R = _R()
+    counts = [9, 0, 140, 3, 70]
+    out = lcb_case(counts, 24, 40, 16, 72, dt, R.ROCS_ACT_NONE, seed=5, ints=True)
+    assert np.array_equal(out["y_c"], out["ref_c"].astype(np.float32))
+    assert np.array_equal(out["y_r"], out["ref_r"].astype(np.float32))
+    assert np.array_equal(out["z"], out["ref_z"].astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_lcb_gather_bit_exact_when_wcc_is_zero(dt):
+    # W_CC = 0 and b = 0: every candidate output is exactly its request's Z row.
+    R = _R()
+    counts = [4, 0, 33, 200, 1]
+    Bc = sum(counts)
+    out = lcb_case(counts, 32, 16, 8, 48, dt, R.ROCS_ACT_NONE, seed=6, bias=False, res=False,
+                   x_c_override=np.zeros((Bc, 16), np.float32))
+    z = out["z"][out["c2r"]]
+    if dt == "bf16":
+        z = to_np(torch.as_tensor(z).to(torch.bfloat16))
+    assert np.array_equal(out["y_c"], z)
+
+
+def test_lcb_request_outputs_bit_identical_across_candidates():
+    # request rows depend only on request inputs: other candidates, other counts -> same bits
+    R = _R()
+    a = lcb_case([1, 500, 2], 64, 64, 32, 32, "bf16", R.ROCS_ACT_RELU, seed=7)
+    b = lcb_case([500, 1, 0], 64, 64, 32, 32, "bf16", R.ROCS_ACT_RELU, seed=7)
+    assert np.array_equal(a["y_r"], b["y_r"])
+    assert np.array_equal(a["z"], b["z"])
+
+
+def test_lcb_candidate_permutation_equivariance():
+    # the candidate half with candidates and map permuted gives permuted rows, bit for bit
+    from request_candidate_sharing_amd import rocs as Rr
+
+    counts = [40, 0, 150, 9]
+    perm = np.random.default_rng(8).permutation(sum(counts))
+    bt = S.make_batch(counts)
+    x_c = rand(np.random.default_rng(1), (sum(counts), 48), True)
+    W = rand(np.random.default_rng(2), (72, 48), True, 0.2)
+    z = torch.randn(len(counts), 72, device="cuda")
+    c2r = torch.as_tensor(bt["cand2req"], device="cuda")
+    c2r_p = torch.as_tensor(bt["cand2req"][perm], device="cuda")
+    xc = dev(x_c, torch.bfloat16)
+    xc_p = dev(x_c[perm], torch.bfloat16)
+    w = dev(W, torch.bfloat16)
+    y1 = torch.empty(sum(counts), 72, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r), Rr.ROCS_BF16, xc, 48, 48, w, None, 72, 1, z,
+                          72, None, 0, y1, 72, Rr.cur_stream())
+    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r_p), Rr.ROCS_BF16, xc_p, 48, 48, w, None, 72, 1,
+                          z, 72, None, 0, y2, 72, Rr.cur_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(y1[perm], y2)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["layer", "rms"])
+@pytest.mark.parametrize("widths", [(72, 136), (512, 512), (1000, 24), (4096, 40)])
+def test_group_norm_parity(dt, kind, widths):
+    R = _R()
+    rng = np.random.default_rng(sum(widths))
+    bf = dt == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    rows_r, rows_c = 37, 301
+    wr, wc = widths
+    x_r, x_c = rand(rng, (rows_r, wr), bf, 2.0), rand(rng, (rows_c, wc), bf, 2.0)
+    res_r, res_c = rand(rng, (rows_r, wr), bf), rand(rng, (rows_c, wc), bf)
+    g_r, b_r = rand(rng, wr, bf), rand(rng, wr, bf)
+    g_c, b_c = rand(rng, wc, bf), rand(rng, wc, bf)
+    esz = 8 if bf else 4
+    ldr, ldc = ((wr + 8 + esz - 1) // esz) * esz, ((wc + 8 + esz - 1) // esz) * esz
+    xr_st, xr = put(x_r, ldr, tdt)
+    xc_st, xc = put(x_c, ldc, tdt)
+    rr_st, rr = put(res_r, ldr, tdt)
+    rc_st, rc = put(res_c, ldc, tdt)
+    _, yr = padded(rows_r, wr, ldr, tdt)
+    _, yc = padded(rows_c, wc, ldc, tdt)
+    k = R.ROCS_NORM_LAYER if kind == "layer" else R.ROCS_NORM_RMS
+    R.rocs_group_norm(R.ROCS_BF16 if bf else R.ROCS_F32, k, 1e-5, rows_r, wr, rows_c, wc, xr, ldr, xc, ldc, rr, rc,
+                      dev(g_r, tdt), dev(b_r, tdt) if kind == "layer" else None, dev(g_c, tdt),
+                      dev(b_c, tdt) if kind == "layer" else None, R.ROCS_ACT_RELU, yr, ldr, yc, ldc, R.cur_stream())
+    torch.cuda.synchronize()
+    for x, r, g, b, y, w in ((x_r, res_r, g_r, b_r, yr, wr), (x_c, res_c, g_c, b_c, yc, wc)):
+        ref = ops.group_norm(x.astype(np.float64) + r, [w], kind, 1e-5, [g], [b] if kind == "layer" else None)
+        assert rel_err(to_np(y), ops.relu(ref)) <= tol(dt)
+
+
+def test_group_norm_in_place_bf16():
+    R = _R()
+    rng = np.random.default_rng(3)
+    x = rand(rng, (50, 512), True, 3.0)
+    t = dev(x, torch.bfloat16)
+    R.rocs_group_norm(R.ROCS_BF16, R.ROCS_NORM_RMS, 1e-5, 0, 0, 50, 512, None, 8, t, 512, None, None, None, None,
+                      None, None, R.ROCS_ACT_NONE, None, 8, t, 512, R.cur_stream())
+    torch.cuda.synchronize()
+    assert rel_err(to_np(t), ops.group_norm(x, [512], "rms")) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_head_parity(dt):
+    R = _R()
+    rng = np.random.default_rng(11)
+    bf = dt == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    counts = [3, 0, 250, 17]
+    bt = S.make_batch(counts)
+    B, Bc, dr, dc = len(counts), sum(counts), 520, 1000
+    x_r, x_c = rand(rng, (B, dr), bf), rand(rng, (Bc, dc), bf)
+    W = rand(rng, (1, dr + dc), bf, (dr + dc) ** -0.5)
+    z = torch.empty(B, dtype=torch.float32, device="cuda")
+    lg = torch.empty(Bc, dtype=torch.float32, device="cuda")
+    R.rocs_head_forward(R.batch(B, Bc, None, torch.as_tensor(bt["cand2req"], device="cuda")),
+                        R.ROCS_BF16 if bf else R.ROCS_F32, dev(x_r, tdt), dr, dr, dev(x_c, tdt), dc, dc,
+                        dev(W[0, :dr], tdt), dev(W[0, dr:], tdt), 0.25, z, lg, R.cur_stream())
+    torch.cuda.synchronize()
+    ref = ops.glm_linear(np.concatenate([x_r[bt["cand2req"]], x_c], 1), W, [0.25], dr, 0)[:, 0]
+    assert rel_err(lg.cpu().numpy(), ref) <= (TOL_F32 if dt == "f32" else 1e-5)
+
+
+def test_broadcast_rows_bit_exact():
+    R = _R()
+    counts = [2, 0, 5, 1, 9]
+    bt = S.make_batch(counts)
+    src = torch.randint(-(2 ** 31), 2 ** 31 - 1, (5, 24), dtype=torch.int32, device="cuda")
+    dst = torch.zeros(sum(counts), 24, dtype=torch.int32, device="cuda")
+    R.rocs_broadcast_rows(R.batch(5, sum(counts), None, torch.as_tensor(bt["cand2req"], device="cuda")), 96, src, 96,
+                          dst, 96, R.cur_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src.cpu()[torch.as_tensor(bt["cand2req"]).long()])
+
+
+def test_validate_batch():
+    R = _R()
+    bt = S.make_batch([3, 0, 2])
+    off = torch.as_tensor(bt["offsets"], device="cuda")
+    c2r = torch.as_tensor(bt["cand2req"], device="cuda")
+    assert R.rocs_validate_batch(R.batch(3, 5, off, c2r), R.cur_stream()) == R.ROCS_OK
+    bad = torch.as_tensor(np.array([0, 0, 2, 1, 2], np.int32), device="cuda")
+    assert R.rocs_validate_batch(R.batch(3, 5, off, bad), R.cur_stream(), check=False) == R.ROCS_ERR_BATCH
+    oob = torch.as_tensor(np.array([0, 0, 0, 7, 2], np.int32), device="cuda")
+    assert R.rocs_validate_batch(R.batch(3, 5, None, oob), R.cur_stream(), check=False) == R.ROCS_ERR_BATCH
+
+
+# ---------------------------------------------------------------- attention
+
+
+def xattn_case(counts, L, H, seed, shuffle=False):
+    R = _R()
+    rng = np.random.default_rng(seed)
+    d = H * 64
+    bt = S.make_batch(counts)
+    B, Bc = len(counts), sum(counts)
+    q_r, q_c = rand(rng, (B, d), True), rand(rng, (Bc, d), True)
+    kv = rand(rng, (B * L, 4 * d), True)  # [K_R | V_R | K_C | V_C] per token
+    m = bt["cand2req"]
+    perm = np.arange(Bc)
+    if shuffle:
+        perm = np.random.default_rng(seed + 1).permutation(Bc)
+    kvt = dev(kv, torch.bfloat16)
+    qr_t, qc_t = dev(q_r, torch.bfloat16), dev(q_c[perm], torch.bfloat16)
+    ar = torch.empty(B, d, dtype=torch.bfloat16, device="cuda")
+    ac = torch.empty(max(Bc, 1), d, dtype=torch.bfloat16, device="cuda")
+    off = None if shuffle else torch.as_tensor(bt["offsets"], device="cuda")
+    c2r = torch.as_tensor(m[perm].astype(np.int32), device="cuda")
+    wsb = R.rocs_dca_cross_attn_workspace_size(B, Bc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    R.rocs_dca_cross_attn(R.batch(B, Bc, off, c2r), R.ROCS_BF16, H, 64, L, qr_t, d, qc_t, d, kvt, kvt[:, d:],
+                          kvt[:, 2 * d:], kvt[:, 3 * d:], 4 * d, 0.0, ar, d, ac, d, ws, wsb, R.cur_stream())
+    torch.cuda.synchronize()
+    K = kv.reshape(B, L, 4 * d)
+    ref_r = ops.attention(q_r[:, None, :], K[:, :, :d], K[:, :, d:2 * d], H)[:, 0]
+    ref_c = ops.attention(q_c[:, None, :], K[m][:, :, 2 * d:3 * d], K[m][:, :, 3 * d:], H)[:, 0]
+    return dict(a_r=to_np(ar), a_c=to_np(ac[:Bc]), ref_r=ref_r, ref_c=ref_c, perm=perm)
+
+
+@pytest.mark.parametrize("counts,L,H", [([5, 0, 130, 300, 1], 200, 2), ([500, 499], 256, 4), ([1] * 7, 64, 1),
+                                        ([260, 3], 1024, 8)])
+def test_cross_attention_parity(counts, L, H):
+    out = xattn_case(counts, L, H, seed=L + H)
+    assert rel_err(out["a_c"], out["ref_c"]) <= TOL_BF16
+    assert rel_err(out["a_r"], out["ref_r"]) <= TOL_BF16
+
+
+def test_cross_attention_shuffled_order_matches_contiguous_bitwise():
+    counts = [40, 0, 131, 7, 300]
+    a = xattn_case(counts, 192, 2, seed=9)
+    b = xattn_case(counts, 192, 2, seed=9, shuffle=True)
+    assert np.array_equal(b["a_c"], a["a_c"][b["perm"]])
+    assert np.array_equal(a["a_r"], b["a_r"])
+
+
+def test_encode_kv_parity():
+    R = _R()
+    cfg = S.small_config(3)
+    inp = S.make_inputs(cfg)
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    st = DeviceStack(inp)
+    B, L, d = cfg.B, cfg.L, cfg.d_seq
+    kv = torch.empty(cfg.n_int * B * L * 4 * d, dtype=torch.bfloat16, device="cuda")
+    wsb = R.rocs_dca_encode_kv_workspace_size(B, L, d, cfg.ffn, cfg.n_enc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    enc, kvw, src = st._dca_arrays
+    R.rocs_dca_encode_kv(R.ROCS_BF16, B, L, d, cfg.n_heads, cfg.ffn, st.seq, cfg.n_enc, enc, cfg.n_int, src, kvw, kv,
+                         ws, wsb, R.cur_stream())
+    torch.cuda.synchronize()
+    ref = oracle.oracle_encoder(inp)
+    got = to_np(kv).reshape(cfg.n_int, B * L, 4 * d)
+    for j in range(cfg.n_int):
+        for q, name in enumerate(("K_R", "V_R", "K_C", "V_C")):
+            r = ref["kv"][j][q].reshape(B * L, d)
+            assert rel_err(got[j][:, q * d:(q + 1) * d], r) <= TOL_BF16, name
+
+
+# ---------------------------------------------------------------- FM / token LCB
+
+
+def test_fm_masked_parity():
+    R = _R()
+    rng = np.random.default_rng(21)
+    counts = [3, 0, 70, 140, 1]
+    bt = S.make_batch(counts)
+    B, Bc, nr, nc, D = len(counts), sum(counts), 32, 16, 128
+    xr, xc = rand(rng, (B, nr, D), True, 0.3), rand(rng, (Bc, nc, D), True, 0.3)
+    fr = torch.empty(B, nr * nr, dtype=torch.bfloat16, device="cuda")
+    fc = torch.empty(Bc, nc * (nr + nc), dtype=torch.bfloat16, device="cuda")
+    R.rocs_fm_masked(R.batch(B, Bc, None, torch.as_tensor(bt["cand2req"], device="cuda")), R.ROCS_BF16, nr, nc, D,
+                     dev(xr.reshape(B, -1), torch.bfloat16), nr * D, dev(xc.reshape(Bc, -1), torch.bfloat16), nc * D,
+                     fr, nr * nr, fc, nc * (nr + nc), R.cur_stream())
+    torch.cuda.synchronize()
+    X = np.concatenate([xr[bt["cand2req"]], xc], 1)
+    ref_r, ref_c = ops.masked_fm(X, nr)
+    assert rel_err(to_np(fc), ref_c) <= TOL_BF16
+    ref_r_req, _ = ops.masked_fm(xr, nr)
+    assert rel_err(to_np(fr), ref_r_req) <= TOL_BF16
+
+
+def test_token_lcb_parity():
+    R = _R()
+    rng = np.random.default_rng(22)
+    counts = [3, 0, 70, 17, 1, 9, 40]
+    bt = S.make_batch(counts)
+    B, Bc, nr, nc, D, tr, tc = len(counts), sum(counts), 32, 16, 128, 64, 64
+    xr, xc = rand(rng, (B, nr, D), True, 0.3), rand(rng, (Bc, nc, D), True, 0.3)
+    W = rand(rng, (tr + tc, nr + nc), True, 48 ** -0.5)
+    yr = torch.empty(B, tr * D, dtype=torch.bfloat16, device="cuda")
+    yc = torch.empty(Bc, tc * D, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(B, tc * D, dtype=torch.float32, device="cuda")
+    R.rocs_token_lcb(R.batch(B, Bc, None, torch.as_tensor(bt["cand2req"], device="cuda")), R.ROCS_BF16, nr, nc, D, tr,
+                     tc, dev(xr.reshape(B, -1), torch.bfloat16), nr * D, dev(xc.reshape(Bc, -1), torch.bfloat16),
+                     nc * D, dev(W[:tr, :nr], torch.bfloat16), dev(W[tr:, :nr], torch.bfloat16),
+                     dev(W[tr:, nr:], torch.bfloat16), yr, tr * D, yc, tc * D, z, R.cur_stream())
+    torch.cuda.synchronize()
+    X = np.concatenate([xr[bt["cand2req"]], xc], 1)
+    ref_r, ref_c = ops.token_lcb(X, W, nr, tr)
+    assert rel_err(to_np(yc), ref_c) <= TOL_BF16
+    ref_r_req, _ = ops.token_lcb(np.concatenate([xr, np.zeros((B, nc, D))], 1), W, nr, tr)
+    assert rel_err(to_np(yr), ref_r_req) <= TOL_BF16
