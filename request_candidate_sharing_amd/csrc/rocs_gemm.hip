@@ -6,28 +6,41 @@
 // reaches HBM.  The request half ([Y_R | Z] = X_R [W_RR; W_CR]^T) is the same
 // kernel with a split output.
 //
-// bf16 path: MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulate.  A workgroup of
-// four waves owns a BM x BN output tile (waves 2 x 2); K advances in 64-wide
-// slabs staged through double-buffered LDS with an XOR swizzle on 16-byte
-// chunks (conflict-free fragment reads).  The MFMA is issued with the weight
-// fragment as the "A" operand so that each lane ends up holding 4
-// consecutive output columns of one output row: the epilogue then reads
-// Z / bias / residual and writes the output with 16-/8-byte accesses.
+// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The weight
+// fragment is the MFMA "A" operand and the activation fragment the "B"
+// operand, so each lane holds 4 consecutive output columns of one output row
+// per register group.  Two kernel families share the instruction, the LDS
+// layout rule and the accumulation order (k16 steps in ascending K):
+//   gemm_bf16_kernel      register-staged loads with element masking at
+//                         every edge (any M; used for request batches);
+//   gemm_bf16_big_kernel  global->LDS DMA (global_load_lds_dwordx4), no
+//                         register staging, zero page for K tails (large M;
+//                         candidate batches).
+// Every output element is therefore reduced in the same order whichever
+// kernel, tile shape or K-slab width computes it: results are bit-identical
+// across batch sizes and batch compositions.
 // Workgroup ids are remapped so that one XCD walks neighbouring tiles.
-//
-// Determinism: every output element is reduced over K in one fixed order
-// (64-wide slabs, two MFMA k-steps each), independent of M, the tile's
-// position and the batch composition.
 #include "rocs_device.h"
 
 namespace rocs {
 
 namespace {
 
-constexpr int BK = 64;  // K slab (two MFMA k-steps of 32)
-
-// 16-byte chunk index inside a [rows][BK] bf16 LDS tile (8 chunks per row).
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// LDS rows hold one K slab of BK bf16 (BK = 64: 8 chunks of 16 B; BK = 32: 4
+// chunks).  Chunk c of row r lives at chunk position c ^ swz(r): fragment
+// reads (32 rows, one chunk column) are conflict-free for both 8-lane
+// (128 B) and 16-lane (256 B) LDS service widths.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64)
+    return (r & 7) ^ ((r >> 3) & 1);
+  else
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
+template <int BK>
+__device__ __forceinline__ int slot(int r, int chunk) {
+  return r * (BK / 8) + (chunk ^ swz<BK>(r));
+}
 
 __device__ __forceinline__ uint4 load_chunk(const bf16* p, int kc, int K) {
   if (kc + 8 <= K) return *reinterpret_cast<const uint4*>(p);
@@ -54,7 +67,9 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
   return to_f(reinterpret_cast<const T*>(p)[i]);
 }
 
-// Epilogue for one output row m and four consecutive columns n..n+3.
+// Epilogue for one output row m and four consecutive columns n..n+3:
+//   v = acc + Z[zrow(m)][n] + bias[n];  v = act(v);  v += res[m][n];  store
+// (columns >= n_split go raw to out1 instead).
 template <typename T>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const float* acc) {
   if (m >= a.M) return;
@@ -121,11 +136,267 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
   }
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int ACH = BM * 8 / 256, WCH = BN * 8 / 256;  // 16-byte chunks per thread per slab
+// Per-wave LDS stage of the transposing epilogue: 32 rows of FN*32 fp32
+// accumulators, rows padded by 16 bytes (conflict-free both ways).
+template <int FN>
+constexpr int stage_pitch() { return FN * 32 + 4; }
+template <int FN>
+constexpr int stage_floats() { return 32 * stage_pitch<FN>(); }
+
+// Writes one wave's 32x32 blocks through the epilogue.  Block (i, j): lane
+// holds row mb + 32i + lane%32 and columns nb + 32j + 8g + 4*(lane/32) + 0..3
+// in registers 4g..4g+3.  Stored directly, every instruction would touch 32
+// rows (half the achievable write bandwidth), so interior tiles pass each
+// block-row of fp32 accumulators through the wave's LDS stage and come back
+// row-contiguous (FN*8 lanes per row, 4 columns each).  All loads of a
+// block-row (map entries, Z rows, residual) are issued before its
+// arithmetic and stores.  The arithmetic is the edge path's: acc + Z + bias,
+// act, + residual, one rounding.
+template <int FM, int FN>
+__device__ __forceinline__ void store_blocks_staged(const GemmArgs& a, int mb, int nb, int lane,
+                                                    f32x16 (&acc)[FM][FN], float* stage) {
+  constexpr int P = stage_pitch<FN>();
+  constexpr int LPR = FN * 8;     // lanes per row
+  constexpr int RPI = 64 / LPR;   // rows per pass
+  constexpr int NP = 32 / RPI;    // passes per block-row
+  const int hk = lane >> 5;
+  const float* __restrict__ z = a.z;
+  const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
+  const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
+  bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
+  const int rl = lane / LPR;
+  const int n = nb + (lane % LPR) * 4;
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias != nullptr) {
+    const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = to_f(bb[e]);
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int mrow0 = mb + i * 32;
+    // map entries and residuals of this lane's NP rows, issued before the LDS round trip
+    int zrow[NP];
+    bf16x4 rr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = min(mrow0 + p * RPI + rl, a.M - 1);
+      zrow[p] = (z != nullptr && a.zmap != nullptr) ? a.zmap[m] : m;
+      if (res != nullptr) rr[p] = *reinterpret_cast<const bf16x4*>(res + int64_t(m) * a.ldres + n);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + j * 32 + 8 * g + 4 * hk) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    __builtin_amdgcn_wave_barrier();
+    float4 zz[NP];
+    if (z != nullptr) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int zr = (unsigned)zrow[p] < (unsigned)a.zrows ? zrow[p] : 0;
+        zz[p] = *reinterpret_cast<const float4*>(z + int64_t(zr) * a.ldz + n);
+      }
+    }
+    f32x4 sv[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = mrow0 + p * RPI + rl;
+      float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
+      if (z != nullptr) {
+        const bool bad = (unsigned)zrow[p] >= (unsigned)a.zrows;
+        v[0] = bad ? nan_f() : v[0] + zz[p].x;
+        v[1] = bad ? nan_f() : v[1] + zz[p].y;
+        v[2] = bad ? nan_f() : v[2] + zz[p].z;
+        v[3] = bad ? nan_f() : v[3] + zz[p].w;
+      }
+      if (bias != nullptr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += bv[e];
+      if (a.act == 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
+      if (res != nullptr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
+      if (m < a.M) {
+        bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
+        *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + n) = pk;
+      }
+    }
+  }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, f32x16 (&acc)[FM][FN],
+                                             float* stage = nullptr) {
+  const int hk = lane >> 5;
+  const bool interior = (nb + FN * 32 <= a.N) && (nb + FN * 32 <= a.n_split) && !a.out0_f32;
+  if (interior && stage != nullptr) {
+    store_blocks_staged(a, mb, nb, lane, acc, stage);
+    return;
+  }
+  if (interior) {
+    const float* __restrict__ z = a.z;
+    const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
+    const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
+    bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = mb + i * 32 + (lane & 31);
+      const bool mok = m < a.M;
+      const int mr = mok ? m : a.M - 1;
+      int zrow = mr;
+      bool bad = false;
+      if (z != nullptr && a.zmap != nullptr) {
+        zrow = a.zmap[mr];
+        bad = (unsigned)zrow >= (unsigned)a.zrows;
+        zrow = bad ? 0 : zrow;
+      }
+      float v[FN][4][4];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[j][g][e] = acc[i][j][4 * g + e];
+      if (z != nullptr) {
+        float4 zz[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            zz[j][g] = *reinterpret_cast<const float4*>(z + int64_t(zrow) * a.ldz + nb + j * 32 + 8 * g + 4 * hk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            v[j][g][0] = bad ? nan_f() : v[j][g][0] + zz[j][g].x;
+            v[j][g][1] = bad ? nan_f() : v[j][g][1] + zz[j][g].y;
+            v[j][g][2] = bad ? nan_f() : v[j][g][2] + zz[j][g].z;
+            v[j][g][3] = bad ? nan_f() : v[j][g][3] + zz[j][g].w;
+          }
+      }
+      if (bias != nullptr) {
+        bf16x4 bb[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) bb[j][g] = *reinterpret_cast<const bf16x4*>(bias + nb + j * 32 + 8 * g + 4 * hk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[j][g][e] += to_f(bb[j][g][e]);
+      }
+      if (a.act == 1)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[j][g][e] = fmaxf(v[j][g][e], 0.f);
+      if (res != nullptr) {
+        bf16x4 rr[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            rr[j][g] = *reinterpret_cast<const bf16x4*>(res + int64_t(mr) * a.ldres + nb + j * 32 + 8 * g + 4 * hk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[j][g][e] += to_f(rr[j][g][e]);
+      }
+      if (mok) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 pk = {to_bf(v[j][g][0]), to_bf(v[j][g][1]), to_bf(v[j][g][2]), to_bf(v[j][g][3])};
+            *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + nb + j * 32 + 8 * g + 4 * hk) = pk;
+          }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = mb + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nb + j * 32 + 8 * g + 4 * hk;
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        epilogue4<bf16>(a, m, n, v);
+      }
+  }
+}
+
+// One BK-wide K slab from LDS: BK/16 k16 steps.  With IL the instruction
+// scheduler is told to interleave the next step's fragment reads with the
+// current step's MFMAs (one DS read after each MFMA), so LDS latency hides
+// behind matrix work inside each wave.
+template <int FM, int FN, int BK, bool IL>
+__device__ __forceinline__ void slab_mfma(const uint4* s, int xr0, int wr0, int hk, f32x16 (&acc)[FM][FN]) {
+  constexpr int KS = BK / 16;
+  bf16x8 xf[2][FM], wf[2][FN];
+  auto frag = [&](int ks, int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) xf[buf][i] = __builtin_bit_cast(bf16x8, s[slot<BK>(xr0 + i * 32, ks * 2 + hk)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wf[buf][j] = __builtin_bit_cast(bf16x8, s[slot<BK>(wr0 + j * 32, ks * 2 + hk)]);
+  };
+  frag(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) frag(ks + 1, (ks + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][j], xf[ks & 1][i], acc[i][j], 0, 0, 0);
+    if constexpr (IL) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int q = 0; q < FM * FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        }
+      }
+    }
+  }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+}
+
+// ----------------------------------------------------------------- register-staged bf16 GEMM
+// WM x WN waves, BM x BN tile, BK = 64; operands staged global -> registers ->
+// LDS with element masking at the M, N and K edges; the next slab's global
+// loads are in flight while the current slab is multiplied.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BK = 64, NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int ACH = BM * 8 / NT, WCH = BN * 8 / NT;  // 16-byte chunks per thread per slab
+  static_assert(ACH * NT == BM * 8 && WCH * NT == BN * 8, "tile rows must divide among threads");
   __shared__ uint4 smem[2][(BM + BN) * 8];
 
   const int ntn = (a.N + BN - 1) / BN;
@@ -137,37 +408,32 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   const bf16* A = reinterpret_cast<const bf16*>(a.A);
   const bf16* aptr[ACH];
   int aslot[ACH], achunk[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int id = tid + i * 256;
+    const int id = tid + i * NT;
     const int r = id >> 3, c = id & 7;
-    const int row = min(m0 + r, a.M - 1);
-    aptr[i] = A + int64_t(row) * a.lda + c * 8;
-    aslot[i] = swz(r, c);
+    aptr[i] = A + int64_t(min(m0 + r, a.M - 1)) * a.lda + c * 8;
+    aslot[i] = slot<BK>(r, c);
     achunk[i] = c * 8;
   }
   const bf16* wptr[WCH];
   int wslot[WCH], wchunk[WCH];
 #pragma unroll
   for (int i = 0; i < WCH; ++i) {
-    const int id = tid + i * 256;
+    const int id = tid + i * NT;
     const int r = id >> 3, c = id & 7;
-    const int row = min(n0 + r, a.N - 1);
-    wptr[i] = weight_row(a, row) + c * 8;
-    wslot[i] = BM * 8 + swz(r, c);
+    wptr[i] = weight_row(a, min(n0 + r, a.N - 1)) + c * 8;
+    wslot[i] = slot<BK>(BM + r, c);
     wchunk[i] = c * 8;
   }
 
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x16 acc[FM][FN];
+  zero_acc(acc);
 
   const int nk = (a.K + BK - 1) / BK;
   uint4 ra[ACH], rw[WCH];
@@ -181,6 +447,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   for (int i = 0; i < WCH; ++i) smem[0][wslot[i]] = rw[i];
   __syncthreads();
 
+  const int xr0 = wm * WTM + (lane & 31);
+  const int wr0 = BM + wn * WTN + (lane & 31);
   for (int kb = 0; kb < nk; ++kb) {
     const int cur = kb & 1;
     const bool more = kb + 1 < nk;
@@ -191,28 +459,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < WCH; ++i) rw[i] = load_chunk(wptr[i] + k0, k0 + wchunk[i], a.K);
     }
-    const uint4* sA = smem[cur];
-    const uint4* sW = smem[cur] + BM * 8;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int chunk = kk * 4 + (lane >> 4);
-      bf16x8 xa[TM], wb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint4 t = sA[swz(wm * WTM + i * 16 + (lane & 15), chunk)];
-        xa[i] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint4 t = sW[swz(wn * WTN + j * 16 + (lane & 15), chunk)];
-        wb[j] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
-    }
+    slab_mfma<FM, FN, BK, false>(smem[cur], xr0, wr0, lane >> 5, acc);
     if (more) {
 #pragma unroll
       for (int i = 0; i < ACH; ++i) smem[cur ^ 1][aslot[i]] = ra[i];
@@ -221,18 +468,89 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
+  static_assert(WM * WN * stage_floats<FN>() * 4 <= int(sizeof(smem)), "epilogue stage exceeds LDS");
+  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
+               reinterpret_cast<float*>(&smem[0][0]) + wave * stage_floats<FN>());
+}
 
-  // lane holds, for tile (i, j): row m0 + wm*WTM + i*16 + lane%16,
-  // columns n0 + wn*WTN + j*16 + 4*(lane/16) + 0..3
+// ----------------------------------------------------------------- DMA-staged bf16 GEMM
+// For the candidate-batch GEMMs (M = B_c in the tens of thousands).  A
+// BM x BN tile per workgroup of WM x WN waves; each wave owns a
+// (BM/WM) x (BN/WN) sub-tile of 32x32 blocks.  Operand slabs (BK wide) move
+// global -> LDS with global_load_lds_dwordx4 (no register staging), double-
+// buffered: the next slab streams in while the current one is multiplied.
+// Each wave-instruction fills 1 KB of LDS (1024 / (2*BK) rows); lane i
+// fetches the global chunk that the row swizzle places at its LDS slot.
+// Chunks past K come from a zero page, so K tails need no masking (K is a
+// multiple of 8: weight and activation rows are 16-byte aligned).
+__device__ uint4 g_zero_page[4];
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN, int WM, int WN, int BK, bool IL, bool STG = true>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;             // rows per wave-instruction
+  constexpr int RB = (BM + BN) / RPI;       // wave-instructions per slab
+  static_assert(RB % NW == 0, "row blocks must divide among waves");
+  constexpr int PER = RB / NW;
+  __shared__ uint4 smem[2][(BM + BN) * CPR];
+
+  const int ntn = (a.N + BN - 1) / BN;
+  const int ntm = (a.M + BM - 1) / BM;
+  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
+  const int m0 = (logical / ntn) * BM;
+  const int n0 = (logical % ntn) * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const bf16* src[PER];
+  int kofs[PER];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WTM + i * 16 + (lane & 15);
+  for (int j = 0; j < PER; ++j) {
+    const int r = (wave * PER + j) * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<BK>(r);
+    kofs[j] = chunk * 8;
+    if (r < BM)
+      src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
+    else
+      src[j] = weight_row(a, min(n0 + r - BM, a.N - 1)) + chunk * 8;
+  }
+  auto issue = [&](int k0, int st) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
-      const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      epilogue4<bf16>(a, m, n, v);
+    for (int j = 0; j < PER; ++j) {
+      const void* p = (k0 + kofs[j] < a.K) ? static_cast<const void*>(src[j] + k0)
+                                          : static_cast<const void*>(g_zero_page);
+      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(&smem[st][(wave * PER + j) * 64]), 16, 0, 0);
     }
+  };
+
+  f32x16 acc[FM][FN];
+  zero_acc(acc);
+
+  const int nk = (a.K + BK - 1) / BK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  const int xr0 = wm * WTM + (lane & 31);
+  const int wr0 = BM + wn * WTN + (lane & 31);
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nk) issue((kb + 1) * BK, cur ^ 1);
+    slab_mfma<FM, FN, BK, IL>(smem[cur], xr0, wr0, lane >> 5, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next slab has landed
+    __syncthreads();
+  }
+  if constexpr (STG) {
+    static_assert(NW * stage_floats<FN>() * 4 <= int(sizeof(smem)), "epilogue stage exceeds LDS");
+    store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
+                 reinterpret_cast<float*>(&smem[0][0]) + wave * stage_floats<FN>());
+  } else {
+    store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
   }
 }
 
@@ -281,25 +599,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i) epilogue4<float>(a, m0 + ty * 4 + i, n0 + tx * 4, acc[i]);
 }
 
+template <typename K>
+hipError_t launch_tiles(K kernel, int bm, int bn, int threads, const GemmArgs& a, hipStream_t s) {
+  const int nwg = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  hipLaunchKernelGGL(kernel, dim3(nwg), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (dt == F32) {
-    const int nwg = ((a.M + 63) / 64) * ((a.N + 63) / 64);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(nwg), dim3(256), 0, s, a);
-    return hipGetLastError();
+  if (dt == F32) return launch_tiles(gemm_f32_kernel, 64, 64, 256, a, s);
+  // All bf16 variants compute every element identically; the choice only
+  // trades tile size against the number of workgroups.
+  // Measured on the candidate shapes (M ~ 7e4): wide outputs favour 128x128
+  // tiles (two workgroups per CU overlap one's epilogue with the other's
+  // main loop), narrow ones 256x256 (fewer operand re-reads from L2).
+  if (a.M >= 2048) {
+    if (a.N > 512) return launch_tiles(gemm_bf16_big_kernel<128, 128, 2, 2, 64, false>, 128, 128, 256, a, s);
+    if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4, 64, false>, 256, 256, 512, a, s);
+    return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2, 64, false>, 256, 128, 512, a, s);
   }
-  // Small-M (request batch) problems use a narrower tile so more workgroups
-  // share the weight stream; the MFMA sequence and K order are identical.
-  if (a.M <= 512) {
-    const int nwg = ((a.M + 63) / 64) * ((a.N + 63) / 64);
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, 64>), dim3(nwg), dim3(256), 0, s, a);
-  } else {
-    const int nwg = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128>), dim3(nwg), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
+  if (a.M > 256) return launch_tiles(gemm_bf16_kernel<128, 128, 2, 2>, 128, 128, 256, a, s);
+  return launch_tiles(gemm_bf16_kernel<64, 64, 2, 2>, 64, 64, 256, a, s);
 }
 
 }  // namespace rocs

@@ -111,6 +111,10 @@ def lcb_case(counts, d_in_r, d_in_c, d_out_r, d_out_c, dt, act, seed, bias=True,
         ([300, 0, 77, 260, 1, 129], (136, 72, 200, 200)),
         ([700, 600], (64, 520, 48, 1000)),
         ([3, 4], (8, 8, 0, 16)),
+        # candidate batches large enough for the 256-row tile kernels, K and N tails
+        ([1200, 0, 1000, 77], (136, 200, 72, 264)),
+        ([2100, 5], (64, 72, 40, 120)),
+        ([3000], (512, 1024, 64, 512)),
     ],
 )
 def test_lcb_forward_parity(dt, counts, dims):
