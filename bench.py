@@ -73,38 +73,56 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
-def candidate_gemm_roofline(st, reps=20):
-    """Times the IKBO candidate GEMM alone: the candidate halves of the stack's
-    GLM linears, launched through rocs_lcb_candidate on torch's current stream
-    and bracketed by events on that stream."""
+ROOFLINE_KERNEL = "gemm_bf16_big_kernel<128, 128, 2, 2, true>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_glm_mlp.json")
+GEMM_SRC = os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", "rocs_gemm.hip")
+
+
+def gemm_source_sha():
+    import hashlib
+
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    only while the kernel source is the one the counters were taken on."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != gemm_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def candidate_gemm_roofline(st, reps=10, sets=3):
+    """Times the dominant kernel alone: the IKBO candidate GEMM of the GLM MLP up
+    projection (x_c [B_c, 512] -> [B_c, 1024], ReLU, Z[m_i] gathered in the
+    epilogue), launched through rocs_lcb_candidate on torch's current stream and
+    bracketed by events on that stream.  Launches rotate over `sets` buffer
+    sets (> 256 MB in total) so the Infinity Cache cannot hold the operands
+    between launches, as in the stack."""
     import torch
     from request_candidate_sharing_amd import rocs as R
 
     cfg = st.cfg
     B_r, B_c = st.B_r, st.B_c
-    d, H = cfg.d_r, cfg.hidden
+    K, N = cfg.d_r, cfg.hidden
     g = torch.Generator(device="cuda").manual_seed(0)
     bf = torch.bfloat16
-    shapes = [(d, H, False), (H, d, True)]  # (K, N, residual)
-    bufs = []
-    for K, N, res in shapes:
-        bufs.append(dict(
-            K=K, N=N, res=res,
-            x=torch.randn(B_c, K, generator=g, device="cuda").to(bf),
-            w=(torch.randn(N, K, generator=g, device="cuda") * K ** -0.5).to(bf),
-            z=torch.randn(B_r, N, generator=g, device="cuda"),
-            r=torch.randn(B_c, N, generator=g, device="cuda").to(bf) if res else None,
-            y=torch.empty(B_c, N, device="cuda", dtype=bf)))
+    w = (torch.randn(N, K, generator=g, device="cuda") * K ** -0.5).to(bf)
+    z = torch.randn(B_r, N, generator=g, device="cuda")
+    bufs = [(torch.randn(B_c, K, generator=g, device="cuda").to(bf), torch.empty(B_c, N, device="cuda", dtype=bf))
+            for _ in range(sets)]
     s = R.cur_stream()
 
     def launch(b):
-        R.rocs_lcb_candidate(st.batch, R.ROCS_BF16, b["x"], b["K"], b["K"], b["w"], None, b["N"],
-                             R.ROCS_ACT_NONE if b["res"] else R.ROCS_ACT_RELU, b["z"], b["N"], b["r"],
-                             b["N"] if b["res"] else 0, b["y"], b["N"], s)
+        R.rocs_lcb_candidate(st.batch, R.ROCS_BF16, b[0], K, K, w, None, N, R.ROCS_ACT_RELU, z, N, None, 0, b[1],
+                             N, s)
 
-    for _ in range(3):
-        for b in bufs:
-            launch(b)
+    for b in bufs:
+        launch(b)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -113,24 +131,37 @@ def candidate_gemm_roofline(st, reps=20):
             launch(b)
     e1.record()
     torch.cuda.synchronize()
-    n = reps * len(bufs)
-    t = e0.elapsed_time(e1) / 1e3 / n
-    flops = np.mean([2.0 * B_c * b["N"] * b["K"] for b in bufs])
-    byts = np.mean([2.0 * B_c * b["K"] + 2.0 * B_c * b["N"] + 2.0 * b["N"] * b["K"] + 4.0 * B_r * b["N"] + 4.0 * B_c
-                    + (2.0 * B_c * b["N"] if b["res"] else 0.0) for b in bufs])
+    t = e0.elapsed_time(e1) / 1e3 / (reps * sets)
+    flops = 2.0 * B_c * N * K
+    # algorithmic bytes: x_c read once, y_c written once, W_CC once, Z (fp32, B_r rows) once, cand2req once
+    byts = 2.0 * B_c * K + 2.0 * B_c * N + 2.0 * N * K + 4.0 * B_r * N + 4.0 * B_c
     t_mfma, t_hbm = flops / PEAK_BF16, byts / PEAK_HBM
     if t_hbm >= t_mfma:
         rf = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     else:
         rf = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
     rf["frac"] = rf["achieved"] / rf["peak"]
-    rf["traffic"] = None
-    rf["kernel"] = "gemm_bf16_kernel<128,128> (rocs_lcb_candidate: IKBO candidate GEMM + Z[m_i] gather epilogue)"
+    rf["traffic"] = measured_traffic(byts)
+    rf["kernel"] = ROOFLINE_KERNEL + " via rocs_lcb_candidate (GLM up projection, B_c x 512 -> B_c x 1024, Z[m_i] epilogue)"
     rf["avg_launch_us"] = t * 1e6
     rf["alg_flops_per_launch"] = flops
     rf["alg_bytes_per_launch"] = byts
     rf["mfma_frac"] = flops / t / PEAK_BF16
+    rf["hbm_frac"] = byts / t / PEAK_HBM
     return rf
+
+
+def copy_calibration(mib=1024, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {mib} MiB")
 
 
 def cpu_baseline(inp, seconds):
@@ -167,7 +198,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-broadcast comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--roofline-reps", type=int, default=10)
+    ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -176,6 +208,11 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calib:
+        torch.cuda.set_device(0)
+        copy_calibration()
+        return
 
     import rocs_synth as S
     from request_candidate_sharing_amd import rocs as R

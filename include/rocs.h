@@ -282,12 +282,26 @@ typedef struct rocs_dca_desc {
   const rocs_kv_w* kvw;                       /* host [n_depths] */
 } rocs_dca_desc;
 
+/* Executor fusion (opt-in).  With ROCS_STACK_FUSE_MLP set, a bf16 stack runs
+ * the pattern
+ *   LINEAR(src=x, dst=h) ; LINEAR(src=h, dst=t [, res=x]) [; NORM(src=t)]
+ * as one fused candidate-side kernel when h (and t, if a NORM follows) is a
+ * workspace slot that no later layer reads, the candidate widths satisfy
+ * d_in % 128 == 0, hidden % 64 == 0, d_out % 32 == 0, d_out <= 512, and the
+ * operands are 16-byte aligned: the hidden activation then never reaches
+ * HBM.  Otherwise, and for request rows always, the layers run unfused.
+ * Without a fused NORM the result is bit-identical to the unfused layers;
+ * with one it differs by the rounding of the pre-norm sum (the unfused path
+ * stores it in the stack dtype first). */
+#define ROCS_STACK_FUSE_MLP 1u
+
 typedef struct rocs_stack_desc {
   rocs_dtype dtype;
   rocs_exec_mode mode;
   int32_t n_slots; const rocs_slot* slots;   /* host [n_slots], n_slots >= 2 */
   int32_t n_layers; const rocs_layer* layers; /* host [n_layers] */
   const rocs_dca_desc* dca;                  /* NULL when no layer is XATTN */
+  uint32_t flags;                            /* ROCS_STACK_* bits */
 } rocs_stack_desc;
 
 typedef struct rocs_stack_io {

@@ -10,7 +10,8 @@
 // fragment is the MFMA "A" operand and the activation fragment the "B"
 // operand, so each lane holds 4 consecutive output columns of one output row
 // per register group.  Two kernel families share the instruction, the LDS
-// layout rule and the accumulation order (k16 steps in ascending K):
+// layout rule and the accumulation order (64-wide K groups in ascending
+// order, four k16 steps per group with the k-sets of slab_mfma below):
 //   gemm_bf16_kernel      register-staged loads with element masking at
 //                         every edge (any M; used for request batches);
 //   gemm_bf16_big_kernel  global->LDS DMA (global_load_lds_dwordx4), no
@@ -20,27 +21,11 @@
 // kernel, tile shape or K-slab width computes it: results are bit-identical
 // across batch sizes and batch compositions.
 // Workgroup ids are remapped so that one XCD walks neighbouring tiles.
-#include "rocs_device.h"
+#include "rocs_mfma.h"
 
 namespace rocs {
 
 namespace {
-
-// LDS rows hold one K slab of BK bf16 (BK = 64: 8 chunks of 16 B; BK = 32: 4
-// chunks).  Chunk c of row r lives at chunk position c ^ swz(r): fragment
-// reads (32 rows, one chunk column) are conflict-free for both 8-lane
-// (128 B) and 16-lane (256 B) LDS service widths.
-template <int BK>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 64)
-    return (r & 7) ^ ((r >> 3) & 1);
-  else
-    return ((r >> 1) ^ (r >> 3)) & 3;
-}
-template <int BK>
-__device__ __forceinline__ int slot(int r, int chunk) {
-  return r * (BK / 8) + (chunk ^ swz<BK>(r));
-}
 
 __device__ __forceinline__ uint4 load_chunk(const bf16* p, int kc, int K) {
   if (kc + 8 <= K) return *reinterpret_cast<const uint4*>(p);
@@ -341,49 +326,11 @@ __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, 
   }
 }
 
-// One BK-wide K slab from LDS: BK/16 k16 steps.  With IL the instruction
-// scheduler is told to interleave the next step's fragment reads with the
-// current step's MFMAs (one DS read after each MFMA), so LDS latency hides
-// behind matrix work inside each wave.
-template <int FM, int FN, int BK, bool IL>
-__device__ __forceinline__ void slab_mfma(const uint4* s, int xr0, int wr0, int hk, f32x16 (&acc)[FM][FN]) {
-  constexpr int KS = BK / 16;
-  bf16x8 xf[2][FM], wf[2][FN];
-  auto frag = [&](int ks, int buf) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) xf[buf][i] = __builtin_bit_cast(bf16x8, s[slot<BK>(xr0 + i * 32, ks * 2 + hk)]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) wf[buf][j] = __builtin_bit_cast(bf16x8, s[slot<BK>(wr0 + j * 32, ks * 2 + hk)]);
-  };
-  frag(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (ks + 1 < KS) frag(ks + 1, (ks + 1) & 1);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][j], xf[ks & 1][i], acc[i][j], 0, 0, 0);
-    if constexpr (IL) {
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int q = 0; q < FM * FN; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-        }
-      }
-    }
-  }
-}
-
+// One 64-wide K slab from the LDS tile s: weights (A operand) at rows wr0,
+// activations (B operand) at rows xr0, four k16 steps in the library's K order.
 template <int FM, int FN>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+__device__ __forceinline__ void slab_mfma(const uint4* s, int xr0, int wr0, int hk, f32x16 (&acc)[FM][FN]) {
+  mfma_steps<FM, FN, 4, 8, 8>(s, wr0, s, xr0, 0, hk, acc);
 }
 
 // ----------------------------------------------------------------- register-staged bf16 GEMM
@@ -418,7 +365,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) 
     const int id = tid + i * NT;
     const int r = id >> 3, c = id & 7;
     aptr[i] = A + int64_t(min(m0 + r, a.M - 1)) * a.lda + c * 8;
-    aslot[i] = slot<BK>(r, c);
+    aslot[i] = slot<8>(r, c);
     achunk[i] = c * 8;
   }
   const bf16* wptr[WCH];
@@ -428,7 +375,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) 
     const int id = tid + i * NT;
     const int r = id >> 3, c = id & 7;
     wptr[i] = weight_row(a, min(n0 + r, a.N - 1)) + c * 8;
-    wslot[i] = slot<BK>(BM + r, c);
+    wslot[i] = slot<8>(BM + r, c);
     wchunk[i] = c * 8;
   }
 
@@ -459,7 +406,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) 
 #pragma unroll
       for (int i = 0; i < WCH; ++i) rw[i] = load_chunk(wptr[i] + k0, k0 + wchunk[i], a.K);
     }
-    slab_mfma<FM, FN, BK, false>(smem[cur], xr0, wr0, lane >> 5, acc);
+    slab_mfma(smem[cur], xr0, wr0, lane >> 5, acc);
     if (more) {
 #pragma unroll
       for (int i = 0; i < ACH; ++i) smem[cur ^ 1][aslot[i]] = ra[i];
@@ -487,8 +434,9 @@ __device__ uint4 g_zero_page[4];
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN, int WM, int WN, int BK, bool IL, bool STG = true>
+template <int BM, int BN, int WM, int WN, bool STG = true>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
+  constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -512,7 +460,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int r = (wave * PER + j) * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz<BK>(r);
+    const int chunk = (lane % CPR) ^ swz<CPR>(r);
     kofs[j] = chunk * 8;
     if (r < BM)
       src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
@@ -541,7 +489,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   for (int kb = 0; kb < nk; ++kb) {
     const int cur = kb & 1;
     if (kb + 1 < nk) issue((kb + 1) * BK, cur ^ 1);
-    slab_mfma<FM, FN, BK, IL>(smem[cur], xr0, wr0, lane >> 5, acc);
+    slab_mfma(smem[cur], xr0, wr0, lane >> 5, acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next slab has landed
     __syncthreads();
   }
@@ -617,9 +565,9 @@ hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
   // tiles (two workgroups per CU overlap one's epilogue with the other's
   // main loop), narrow ones 256x256 (fewer operand re-reads from L2).
   if (a.M >= 2048) {
-    if (a.N > 512) return launch_tiles(gemm_bf16_big_kernel<128, 128, 2, 2, 64, false>, 128, 128, 256, a, s);
-    if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4, 64, false>, 256, 256, 512, a, s);
-    return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2, 64, false>, 256, 128, 512, a, s);
+    if (a.N > 512) return launch_tiles(gemm_bf16_big_kernel<128, 128, 2, 2>, 128, 128, 256, a, s);
+    if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);
+    return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2>, 256, 128, 512, a, s);
   }
   if (a.M > 256) return launch_tiles(gemm_bf16_kernel<128, 128, 2, 2>, 128, 128, 256, a, s);
   return launch_tiles(gemm_bf16_kernel<64, 64, 2, 2>, 64, 64, 256, a, s);

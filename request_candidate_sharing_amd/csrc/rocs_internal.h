@@ -153,6 +153,35 @@ struct TokLcbArgs {
 hipError_t launch_token_lcb_request(const TokLcbArgs& a, hipStream_t s);
 hipError_t launch_token_lcb_candidate(const TokLcbArgs& a, hipStream_t s);
 
+// Fused candidate-side GLM MLP block (see rocs_mlp.hip):
+//   y = norm(act2(act1(x W1^T + Z1[zrow] + b1) W2^T + Z2[zrow] + b2) + x?)
+struct MlpArgs {
+  int M, d_in, hidden, d_out;
+  const bf16* x;
+  int64_t ldx;
+  const bf16* w1;  // [hidden, d_in]
+  const bf16* b1;  // [hidden] or null
+  const float* z1;
+  int64_t ldz1;
+  int act1;
+  const bf16* w2;  // [d_out, hidden]
+  const bf16* b2;  // [d_out] or null
+  const float* z2;
+  int64_t ldz2;
+  int act2;
+  const int32_t* zmap;  // null: Z rows are candidate rows
+  int zrows;
+  int residual;  // add x (d_in == d_out)
+  int norm;      // -1 none, 0 LayerNorm, 1 RMSNorm (statistics over d_out)
+  float eps;
+  const bf16* gamma;
+  const bf16* beta;
+  bf16* y;
+  int64_t ldy;
+};
+bool mlp_block_supported(int d_in, int hidden, int d_out);
+hipError_t launch_mlp_block(const MlpArgs& a, hipStream_t s);
+
 hipError_t launch_validate_batch(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, int32_t* flag,
                                  hipStream_t s);
 

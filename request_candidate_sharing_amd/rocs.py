@@ -81,7 +81,11 @@ class rocs_stack_desc(ctypes.Structure):
         ("n_slots", c_int32), ("slots", ctypes.POINTER(rocs_slot)),
         ("n_layers", c_int32), ("layers", ctypes.POINTER(rocs_layer)),
         ("dca", ctypes.POINTER(rocs_dca_desc)),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+ROCS_STACK_FUSE_MLP = 1
 
 
 class rocs_stack_io(ctypes.Structure):

@@ -37,7 +37,8 @@ def _torch():
 class DeviceStack:
     """One workload's inputs, weights, descriptor and outputs on a GPU."""
 
-    def __init__(self, inputs: Dict[str, Any], device="cuda", mode: int = R.ROCS_EXEC_SHARED):
+    def __init__(self, inputs: Dict[str, Any], device="cuda", mode: int = R.ROCS_EXEC_SHARED, fusion: bool = False):
+        self.flags = R.ROCS_STACK_FUSE_MLP if fusion else 0
         torch = _torch()
         self.torch = torch
         self.inputs = inputs
@@ -208,7 +209,7 @@ class DeviceStack:
         self._slot_arr = (R.rocs_slot * n)(*[R.rocs_slot(a, b) for a, b in self.slots])
         self._layer_arr = (R.rocs_layer * len(self.layers))(*self.layers)
         self.desc = R.rocs_stack_desc(self.rdt, self.mode, n, self._slot_arr, len(self.layers), self._layer_arr,
-                                      ctypes.pointer(self.dca) if self.dca is not None else None)
+                                      ctypes.pointer(self.dca) if self.dca is not None else None, self.flags)
         wr1, wc1 = self.slots[1]
         self.y_r = torch.empty((self.B_r, wr1), dtype=self.tdt, device=self.device)
         self.y_c = torch.empty((max(self.B_c, 1), wc1), dtype=self.tdt, device=self.device)

@@ -159,7 +159,7 @@ def small_config(k: int) -> StackConfig:
     if k == 1:
         return c
     if k == 2:
-        return c.with_(B=12, counts=("uniform", 0, 150), d_r=136, d_c=72, hidden=200, n_blocks=2)
+        return c.with_(B=12, counts=("uniform", 0, 150), d_r=136, d_c=128, hidden=320, n_blocks=2)
     if k == 3:
         return c.with_(B=5, counts=("uniform", 0, 140), d_r=128, d_c=64, hidden=256, L=200, d_seq=128,
                        n_heads=2, ffn=512, n_enc=2, n_int=1)

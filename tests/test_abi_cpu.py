@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports what include/rocs.h
+declares, and its host-side argument checks return the documented status
+codes before any device work (so only invalid calls are made here: a valid
+one would launch kernels)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from request_candidate_sharing_amd import rocs as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rocs.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(R.LIB_PATH), reason="librocs not built")
+
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(rocs_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def header_define(name):
+    """Value of a #define or an enumerator in the header."""
+    text = open(HEADER).read()
+    m = re.search(rf"#define\s+{name}\s+(-?\w+)", text) or re.search(rf"\b{name}\s*=\s*(-?\w+)", text)
+    return int(m.group(1).rstrip("u"), 0)
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for required in ("rocs_lcb_request", "rocs_lcb_candidate", "rocs_stack_forward", "rocs_dca_cross_attn",
+                     "rocs_fm_masked", "rocs_token_lcb", "rocs_group_norm", "rocs_head_forward"):
+        assert required in names
+
+
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(R.LIB_PATH)
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding covers exactly the header's functions
+    assert sorted(R.EXPORTED) == header_functions()
+
+
+def test_status_codes_and_version_match_header():
+    for name in ("ROCS_OK", "ROCS_ERR_INVALID_ARG", "ROCS_ERR_SHAPE", "ROCS_ERR_DTYPE", "ROCS_ERR_ALIGN",
+                 "ROCS_ERR_WORKSPACE", "ROCS_ERR_BATCH", "ROCS_ERR_HIP", "ROCS_ERR_UNSUPPORTED"):
+        code = header_define(name)
+        assert getattr(R, name) == code
+        assert R.status_name(code) == name
+    assert R.rocs_version() == header_define("ROCS_VERSION")
+    assert R.ROCS_STACK_FUSE_MLP == header_define("ROCS_STACK_FUSE_MLP")
+
+
+def _lcb_request(**kw):
+    a = dict(dtype=R.ROCS_BF16, B_r=4, x_r=FAKE, ld_xr=64, d_in_r=64, w_rr=FAKE, w_cr=FAKE, b_r=None, d_out_r=64,
+             d_out_c=64, act=R.ROCS_ACT_NONE, res_r=None, ld_resr=0, y_r=FAKE, ld_yr=64, z=FAKE, ld_z=64)
+    a.update(kw)
+    return R.rocs_lcb_request(**a, stream=None, check=False)
+
+
+def test_lcb_request_argument_checks():
+    assert _lcb_request(x_r=None) == R.ROCS_ERR_INVALID_ARG
+    assert "x_r" in R.last_error()
+    assert _lcb_request(x_r=FAKE + 2) == R.ROCS_ERR_ALIGN
+    assert _lcb_request(ld_xr=32) == R.ROCS_ERR_SHAPE
+    assert _lcb_request(dtype=7) == R.ROCS_ERR_INVALID_ARG  # unknown dtype
+    assert _lcb_request(B_r=-1) != R.ROCS_OK
+    assert _lcb_request(w_cr=None) == R.ROCS_ERR_INVALID_ARG
+
+
+def test_bf16_only_calls_reject_f32():
+    b = R.batch(2, 6, None, FAKE)
+    st = R.rocs_dca_cross_attn(b, R.ROCS_F32, 2, 64, 32, FAKE, 128, FAKE, 128, FAKE, FAKE, FAKE, FAKE, 512, 0.125,
+                               FAKE, 128, FAKE, 128, FAKE, 1 << 20, check=False)
+    assert st == R.ROCS_ERR_DTYPE
+
+
+def test_batch_checks():
+    b = R.batch(0, 5, None, FAKE)
+    st = R.rocs_lcb_candidate(b, R.ROCS_BF16, FAKE, 64, 64, FAKE, None, 64, 0, FAKE, 64, None, 0, FAKE, 64,
+                              check=False)
+    assert st == R.ROCS_ERR_BATCH
+    b = R.batch(2, 5, None, None)
+    st = R.rocs_lcb_candidate(b, R.ROCS_BF16, FAKE, 64, 64, FAKE, None, 64, 0, FAKE, 64, None, 0, FAKE, 64,
+                              check=False)
+    assert st == R.ROCS_ERR_INVALID_ARG and "cand2req" in R.last_error()
+    assert R.rocs_validate_batch(R.batch(-1, 0), check=False) != R.ROCS_OK
+
+
+def _glm_mlp_desc(d=512, H=1024, n_blocks=3, bad_src=False):
+    """A host descriptor of the GLM MLP stack (fake weight addresses)."""
+    slots = (R.rocs_slot * 4)(R.rocs_slot(d, d), R.rocs_slot(d, d), R.rocs_slot(H, H), R.rocs_slot(d, d))
+    layers = []
+
+    def lin(src, dst, din, dout, act=0, res=-1):
+        L = R.rocs_layer()
+        L.kind, L.src, L.dst, L.res = R.ROCS_OP_LINEAR, src, dst, res
+        L.d_in_r = L.d_in_c = din
+        L.d_out_r = L.d_out_c = dout
+        L.act = act
+        L.w_rr = L.w_cr = L.w_cc = FAKE
+        layers.append(L)
+
+    cur = 0
+    for _ in range(n_blocks):
+        lin(cur, 2, d, H, act=R.ROCS_ACT_RELU)
+        lin(2, 3, H, d, res=cur)
+        N = R.rocs_layer()
+        N.kind, N.src, N.dst, N.res, N.d_in_r, N.d_in_c, N.norm, N.eps = R.ROCS_OP_NORM, 3, 1, -1, d, d, 1, 1e-6
+        layers.append(N)
+        cur = 1
+    Hd = R.rocs_layer()
+    Hd.kind, Hd.src, Hd.res, Hd.d_in_r, Hd.d_in_c, Hd.d_out_c, Hd.w_cr, Hd.w_cc = R.ROCS_OP_HEAD, 1, -1, d, d, 1, FAKE, FAKE
+    layers.append(Hd)
+    if bad_src:
+        layers[1].src = 9
+    arr = (R.rocs_layer * len(layers))(*layers)
+    desc = R.rocs_stack_desc(R.ROCS_BF16, R.ROCS_EXEC_SHARED, 4, slots, len(layers), arr, None, 0)
+    desc._keep = (slots, arr)
+    return desc
+
+
+def test_stack_workspace_size_is_host_logic():
+    desc = _glm_mlp_desc()
+    small = R.rocs_stack_workspace_size(desc, 4, 100)
+    big = R.rocs_stack_workspace_size(desc, 256, 73704)
+    assert 0 < small < big
+    # the hidden slot alone: 73704 candidates x 1024 bf16, plus the fp32 Z of 256 requests
+    assert big >= 73704 * 1024 * 2 + 256 * 1024 * 4
+    assert R.rocs_stack_workspace_size(desc, -1, 5) == 0
+
+
+def test_stack_descriptor_errors():
+    desc = _glm_mlp_desc(bad_src=True)
+    assert R.rocs_stack_workspace_size(desc, 4, 100) == 0
+    assert "out of range" in R.last_error()
+    b = R.batch(1, 0)
+    io = R.rocs_stack_io()
+    st = R.rocs_stack_forward(desc, b, io, None, 0, check=False)
+    assert st == R.ROCS_ERR_INVALID_ARG
+
+
+def test_stack_forward_checks_workspace_before_launch():
+    desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
+    io = R.rocs_stack_io(FAKE, 128, FAKE, 128, FAKE, 128, FAKE, 128, None, FAKE)
+    b = R.batch(2, 6, None, FAKE)
+    need = R.rocs_stack_workspace_size(desc, 2, 6)
+    st = R.rocs_stack_forward(desc, b, io, FAKE, need - 1, check=False)
+    assert st == R.ROCS_ERR_WORKSPACE
+    st = R.rocs_stack_forward(desc, b, io, None, need, check=False)
+    assert st == R.ROCS_ERR_WORKSPACE
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(R.RocsError) as e:
+        R.rocs_lcb_request(R.ROCS_BF16, 4, None, 64, 64, FAKE, FAKE, None, 64, 64, 0, None, 0, FAKE, 64, FAKE, 64)
+    assert "x_r" in str(e.value)

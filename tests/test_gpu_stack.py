@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def _stack(inp, mode=0):
+def _stack(inp, mode=0, fusion=False):
     from request_candidate_sharing_amd.stacks import DeviceStack
 
-    st = DeviceStack(inp, mode=mode)
+    st = DeviceStack(inp, mode=mode, fusion=fusion)
     st.run()
     return st, st.outputs()
 
@@ -86,6 +86,37 @@ def test_dense_broadcast_mode_matches_shared(k):
     assert np.array_equal(a["y_r"], b["y_r"])
 
 
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_fused_stack_parity(k):
+    # ROCS_STACK_FUSE_MLP: candidate-side LINEAR -> LINEAR [-> NORM] as one kernel
+    # (GLM MLP blocks of workload 2, the 256-wide interaction MLPs of the DCA stacks).
+    cfg = S.small_config(k)
+    inp = S.make_inputs(cfg)
+    _, got = _stack(inp, fusion=True)
+    _compare(cfg, got, oracle.oracle_forward(inp))
+
+
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_fused_mlp_block_matches_unfused_layers(k):
+    # Without a fused norm (the DCA interaction MLPs) both paths reduce in the same
+    # order and round once: identical bits.  With the norm fused (workload 2), the
+    # unfused path rounds the pre-norm sum to bf16 first.
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    cfg = S.small_config(k)
+    inp = S.make_inputs(cfg)
+    f = DeviceStack(inp, fusion=True)
+    u = DeviceStack(inp, fusion=False)
+    f.run()
+    u.run()
+    a, b = f.outputs(), u.outputs()
+    assert np.array_equal(a["y_r"], b["y_r"])
+    if k == 2:
+        assert rel_err(a["y_c"], b["y_c"]) <= 1e-2
+    else:
+        assert np.array_equal(a["y_c"], b["y_c"])
+
+
 def test_single_candidate_requests_match_oracle():
     cfg = S.small_config(2)
     inp = S.make_inputs(cfg, counts=[1] * cfg.B)
@@ -101,11 +132,12 @@ def test_tiny_glm_full_fp32():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("k,sample", [(2, [0, 77, 255]), (3, [0, 63]), (4, [5, 100]), (5, [0, 31])])
-def test_full_size_stack_sampled(k, sample):
+@pytest.mark.parametrize("k,sample,fusion", [(2, [0, 77, 255], False), (2, [3, 128], True), (3, [0, 63], False),
+                                            (4, [5, 100], False), (5, [0, 31], False)])
+def test_full_size_stack_sampled(k, sample, fusion):
     cfg = S.config(k)
     inp = S.make_inputs(cfg)
-    _, got = _stack(inp)
+    _, got = _stack(inp, fusion=fusion)
     assert np.all(np.isfinite(got["y_c"]))
     ref = oracle.oracle_forward(inp, requests=sample)
     _compare(cfg, got, ref, rows=ref["rows"], reqs=ref["requests"])
