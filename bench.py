@@ -75,13 +75,18 @@ def time_steps(fn, steps, warmup):
 
 ROOFLINE_KERNEL = "gemm_bf16_big_kernel<128, 128, 2, 2, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_glm_mlp.json")
-GEMM_SRC = os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", "rocs_gemm.hip")
+# sources the candidate GEMM is compiled from (the counters are void once any of them changes)
+GEMM_SRCS = [os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", f)
+             for f in ("rocs_gemm.hip", "rocs_mfma.h", "rocs_device.h")]
 
 
 def gemm_source_sha():
     import hashlib
 
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(alg_bytes):

@@ -423,18 +423,28 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) 
 // ----------------------------------------------------------------- DMA-staged bf16 GEMM
 // For the candidate-batch GEMMs (M = B_c in the tens of thousands).  A
 // BM x BN tile per workgroup of WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 blocks.  Operand slabs (BK wide) move
-// global -> LDS with global_load_lds_dwordx4 (no register staging), double-
-// buffered: the next slab streams in while the current one is multiplied.
-// Each wave-instruction fills 1 KB of LDS (1024 / (2*BK) rows); lane i
-// fetches the global chunk that the row swizzle places at its LDS slot.
-// Chunks past K come from a zero page, so K tails need no masking (K is a
-// multiple of 8: weight and activation rows are 16-byte aligned).
+// (BM/WM) x (BN/WN) sub-tile of 32x32 blocks.  Operand slabs (64 wide in K)
+// move global -> LDS with global_load_lds_dwordx4 (no register staging)
+// through a ring of NS slab buffers: NS-1 slabs are in flight while one is
+// multiplied, which hides the HBM latency of the activation rows (each slab
+// of a 512-deep K is a fresh HBM read).  Each wave-instruction fills 1 KB of
+// LDS (8 rows of 128 B); lane i fetches the global chunk that the row
+// swizzle places at its LDS slot.  Chunks past K come from a zero page, so K
+// tails need no masking (K is a multiple of 8: weight and activation rows
+// are 16-byte aligned).
 __device__ uint4 g_zero_page[4];
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN, int WM, int WN, bool STG = true>
+// s_waitcnt with vmcnt(N), expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int WM, int WN, int NS = 2, bool STG = true>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
@@ -445,7 +455,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   constexpr int RB = (BM + BN) / RPI;       // wave-instructions per slab
   static_assert(RB % NW == 0, "row blocks must divide among waves");
   constexpr int PER = RB / NW;
-  __shared__ uint4 smem[2][(BM + BN) * CPR];
+  static_assert(NS >= 2 && PER * (NS - 2) < 64, "ring depth");
+  __shared__ uint4 smem[NS][(BM + BN) * CPR];
 
   const int ntn = (a.N + BN - 1) / BN;
   const int ntm = (a.M + BM - 1) / BM;
@@ -480,19 +491,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   zero_acc(acc);
 
   const int nk = (a.K + BK - 1) / BK;
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s * BK, s);
 
   const int xr0 = wm * WTM + (lane & 31);
   const int wr0 = BM + wn * WTN + (lane & 31);
   for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nk) issue((kb + 1) * BK, cur ^ 1);
-    slab_mfma(smem[cur], xr0, wr0, lane >> 5, acc);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next slab has landed
+    // Slab kb has landed once at most min(NS-2, nk-1-kb) newer slabs (PER
+    // instructions each, returned in order) are still outstanding.
+    const int newer = min(NS - 2, nk - 1 - kb);
+    if constexpr (NS >= 4) {
+      if (newer >= 2) wait_vmcnt<PER * 2>();
+      else if (newer == 1) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NS == 3) {
+      if (newer >= 1) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // every wave's part of slab kb is in LDS, and every wave is done with
+    // slab kb-1, whose buffer the next issue refills
     __syncthreads();
+    if (kb + NS - 1 < nk) issue((kb + NS - 1) * BK, (kb + NS - 1) % NS);
+    slab_mfma(smem[kb % NS], xr0, wr0, lane >> 5, acc);
   }
+  wait_vmcnt<0>();
+  __syncthreads();  // the epilogue reuses the ring as its staging buffer
   if constexpr (STG) {
     static_assert(NW * stage_floats<FN>() * 4 <= int(sizeof(smem)), "epilogue stage exceeds LDS");
     store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,

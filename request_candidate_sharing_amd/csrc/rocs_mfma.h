@@ -73,6 +73,10 @@ __device__ __forceinline__ void mfma_steps(const uint4* sa, int ar0, const uint4
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (ks + 1 < KS) frag(ks + 1, (ks + 1) & 1);
+    // Keep the next step's LDS reads ahead of this step's MFMAs: left alone,
+    // the scheduler sinks each read next to its first use, which exposes the
+    // LDS latency at every step.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
