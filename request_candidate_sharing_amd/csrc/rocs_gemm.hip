@@ -586,12 +586,11 @@ hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (dt == F32) return launch_tiles(gemm_f32_kernel, 64, 64, 256, a, s);
   // All bf16 variants compute every element identically; the choice only
-  // trades tile size against the number of workgroups.
-  // Measured on the candidate shapes (M ~ 7e4): wide outputs favour 128x128
-  // tiles (two workgroups per CU overlap one's epilogue with the other's
-  // main loop), narrow ones 256x256 (fewer operand re-reads from L2).
+  // trades tile size against the number of workgroups.  Measured on the
+  // candidate shapes (M = 73,704; K, N = 512/1024 both ways, interleaved
+  // medians): 256x256 tiles beat 128x128 ones (139 vs 164 us for N = 1024,
+  // 136 vs 137 us for N = 512): half the operand traffic from L2 per FLOP.
   if (a.M >= 2048) {
-    if (a.N > 512) return launch_tiles(gemm_bf16_big_kernel<128, 128, 2, 2>, 128, 128, 256, a, s);
     if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);
     return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2>, 256, 128, 512, a, s);
   }

@@ -115,6 +115,8 @@ def lcb_case(counts, d_in_r, d_in_c, d_out_r, d_out_c, dt, act, seed, bias=True,
         ([1200, 0, 1000, 77], (136, 200, 72, 264)),
         ([2100, 5], (64, 72, 40, 120)),
         ([3000], (512, 1024, 64, 512)),
+        # many tiny requests: a 256-row tile spans more request rows than it stages in LDS
+        ([3] * 700 + [0, 1] * 40, (64, 128, 32, 384)),
     ],
 )
 def test_lcb_forward_parity(dt, counts, dims):
@@ -160,29 +162,34 @@ def test_lcb_request_outputs_bit_identical_across_candidates():
     assert np.array_equal(a["z"], b["z"])
 
 
-def test_lcb_candidate_permutation_equivariance():
+@pytest.mark.parametrize("counts,K,N", [([40, 0, 150, 9], 48, 72),
+                                        # large batches: grouped candidates stage Z rows in LDS, shuffled ones gather them
+                                        ([1500, 40, 0, 900, 3], 136, 264),
+                                        ([2500, 700], 512, 512)])
+def test_lcb_candidate_permutation_equivariance(counts, K, N):
     # the candidate half with candidates and map permuted gives permuted rows, bit for bit
     from request_candidate_sharing_amd import rocs as Rr
 
-    counts = [40, 0, 150, 9]
     perm = np.random.default_rng(8).permutation(sum(counts))
     bt = S.make_batch(counts)
-    x_c = rand(np.random.default_rng(1), (sum(counts), 48), True)
-    W = rand(np.random.default_rng(2), (72, 48), True, 0.2)
-    z = torch.randn(len(counts), 72, device="cuda")
+    x_c = rand(np.random.default_rng(1), (sum(counts), K), True)
+    W = rand(np.random.default_rng(2), (N, K), True, K ** -0.5)
+    z = torch.randn(len(counts), N, device="cuda")
+    b = dev(rand(np.random.default_rng(3), N, True, 0.5), torch.bfloat16)
+    res = dev(rand(np.random.default_rng(4), (sum(counts), N), True), torch.bfloat16)
     c2r = torch.as_tensor(bt["cand2req"], device="cuda")
     c2r_p = torch.as_tensor(bt["cand2req"][perm], device="cuda")
+    pt = torch.as_tensor(perm, device="cuda")
     xc = dev(x_c, torch.bfloat16)
-    xc_p = dev(x_c[perm], torch.bfloat16)
     w = dev(W, torch.bfloat16)
-    y1 = torch.empty(sum(counts), 72, dtype=torch.bfloat16, device="cuda")
+    y1 = torch.empty(sum(counts), N, dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty_like(y1)
-    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r), Rr.ROCS_BF16, xc, 48, 48, w, None, 72, 1, z,
-                          72, None, 0, y1, 72, Rr.cur_stream())
-    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r_p), Rr.ROCS_BF16, xc_p, 48, 48, w, None, 72, 1,
-                          z, 72, None, 0, y2, 72, Rr.cur_stream())
+    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r), Rr.ROCS_BF16, xc, K, K, w, b, N, 1, z,
+                          N, res, N, y1, N, Rr.cur_stream())
+    Rr.rocs_lcb_candidate(Rr.batch(len(counts), sum(counts), None, c2r_p), Rr.ROCS_BF16, xc[pt].contiguous(), K, K, w,
+                          b, N, 1, z, N, res[pt].contiguous(), N, y2, N, Rr.cur_stream())
     torch.cuda.synchronize()
-    assert torch.equal(y1[perm], y2)
+    assert torch.equal(y1[pt], y2)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
