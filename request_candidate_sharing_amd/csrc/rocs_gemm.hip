@@ -444,6 +444,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Wait until at most `newer` slabs of PER instructions each are outstanding
+// (0 <= newer <= MAXN; the immediate must be a compile-time constant).
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_slabs(int newer) {
+  if constexpr (MAXN > 0) {
+    if (newer >= MAXN) {
+      wait_vmcnt<PER * MAXN>();
+      return;
+    }
+    wait_slabs<PER, MAXN - 1>(newer);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int NS = 2, bool STG = true>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
   constexpr int BK = 64;
@@ -500,17 +515,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   for (int kb = 0; kb < nk; ++kb) {
     // Slab kb has landed once at most min(NS-2, nk-1-kb) newer slabs (PER
     // instructions each, returned in order) are still outstanding.
-    const int newer = min(NS - 2, nk - 1 - kb);
-    if constexpr (NS >= 4) {
-      if (newer >= 2) wait_vmcnt<PER * 2>();
-      else if (newer == 1) wait_vmcnt<PER>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NS == 3) {
-      if (newer >= 1) wait_vmcnt<PER>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_slabs<PER, NS - 2>(min(NS - 2, nk - 1 - kb));
     // every wave's part of slab kb is in LDS, and every wave is done with
     // slab kb-1, whose buffer the next issue refills
     __syncthreads();
@@ -594,8 +599,11 @@ hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
     if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);
     return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2>, 256, 128, 512, a, s);
   }
-  if (a.M > 256) return launch_tiles(gemm_bf16_kernel<128, 128, 2, 2>, 128, 128, 256, a, s);
-  return launch_tiles(gemm_bf16_kernel<64, 64, 2, 2>, 64, 64, 256, a, s);
+  // Request batches (M <= a few hundred): the weights stream from HBM once
+  // and K/64 slabs run in sequence, so the time is slab latency.  One-wave
+  // 32x32 tiles put enough workgroups on the chip (B_r = 256, N = 1024:
+  // 256 of them), each with seven slabs (56 KB) in flight.
+  return launch_tiles(gemm_bf16_big_kernel<32, 32, 1, 1, 8>, 32, 32, 64, a, s);
 }
 
 }  // namespace rocs
