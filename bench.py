@@ -195,6 +195,29 @@ def cpu_baseline(inp, seconds):
                       f"of the same batch: {done} candidates in {t_total:.1f} s"}
 
 
+def other_workload(args):
+    """Shared (and dense-broadcast) step time of another workload's stack, for profiling."""
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    cfg = S.config(args.workload)
+    inp = S.make_inputs(cfg)
+    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+    log(f"bench: workload {args.workload} ({cfg.name()}) B_r={B_r} B_c={B_c}")
+    st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+    t_sh, _ = time_steps(st.run, args.steps, args.warmup)
+    del st
+    out = {"workload": args.workload, "name": cfg.name(), "B_r": B_r, "B_c": B_c,
+           "ms_per_step": t_sh / args.steps * 1e3, "candidates_per_s": B_c * args.steps / t_sh}
+    if not args.no_dense:
+        de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+        t_de, _ = time_steps(de.run, args.steps, args.warmup)
+        out["dense_broadcast_ms_per_step"] = t_de / args.steps * 1e3
+        out["speedup_vs_dense_broadcast"] = t_de / t_sh
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +228,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--roofline-reps", type=int, default=10)
     ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="profiling aid: time another workload's stack (1-5); the benchmark line is workload 2")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -224,6 +249,8 @@ def main():
     from request_candidate_sharing_amd.stacks import DeviceStack
 
     torch.cuda.set_device(0)
+    if args.workload != 2:
+        return other_workload(args)
     cfg = S.config(2)
     inp = S.make_inputs(cfg)
     B_r, B_c = cfg.B, int(len(inp["cand2req"]))
