@@ -220,9 +220,13 @@ int rocs_dca_encode_kv(rocs_dtype dtype, int32_t B_r, int32_t L, int32_t d, int3
  * q_c [B_c, H*64] (ld_qc); outputs a_r (ld_ar), a_c (ld_ac).  q_r/a_r
  * nullable (skip the request group).  bf16 only, head_dim == 64,
  * scale <= 0 selects 1/sqrt(head_dim).  workspace >=
- * rocs_dca_cross_attn_workspace_size(B_r, B_c) (per-request query tiles
- * and, when batch->offsets is NULL, a device counting sort of cand2req). */
-size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c);
+ * rocs_dca_cross_attn_workspace_size(B_r, B_c, n_heads, L): per-request
+ * query tiles, a device counting sort of cand2req when batch->offsets is
+ * NULL, and V_R^T / V_C^T staged once per call (keys contiguous per head
+ * dimension, the layout the PV product reads), so that the query tiles of
+ * one request do not each transpose the same values.  Needed whenever
+ * there are candidates or request queries. */
+size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c, int32_t n_heads, int32_t L);
 int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim, int32_t L,
                         const void* q_r, int64_t ld_qr, const void* q_c, int64_t ld_qc, const void* k_r,
                         const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv, float scale, void* a_r,

@@ -231,6 +231,9 @@ int lcb_candidate_launch(int B_c, int B_r, const int32_t* zmap, rocs_dtype dt, c
 
 // ------------------------------------------------------------------ DCA helpers
 
+// V^T staging of B sequences of L keys, d = H*64 columns (attention PV operand)
+size_t vt_bytes(int B, int L, int d) { return align_up(size_t(B) * d * size_t(vt_pad(L)) * 2, 256); }
+
 size_t enc_ws_bytes(int B_r, int L, int d, int ffn, int n_enc) {
   const size_t rows = size_t(B_r) * L;
   size_t b = 0;
@@ -238,6 +241,7 @@ size_t enc_ws_bytes(int B_r, int L, int d, int ffn, int n_enc) {
   b += align_up(rows * 3 * d * 2, 256);              // qkv
   b += align_up(rows * d * 2, 256) * 2;              // attention output, residual sum
   b += align_up(rows * size_t(ffn) * 2, 256);        // FFN hidden
+  b += vt_bytes(B_r, L, d);                          // V^T of the self-attention
   return b;
 }
 
@@ -336,6 +340,8 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
   bf16* tmp = reinterpret_cast<bf16*>(w);
   w += align_up(size_t(rows) * d * 2, 256);
   bf16* hid = reinterpret_cast<bf16*>(w);
+  w += align_up(size_t(rows) * size_t(ffn) * 2, 256);
+  bf16* vt = reinterpret_cast<bf16*>(w);
 
   for (int k = 0; k < n_enc; ++k) {
     const rocs_enc_layer& e = enc[k];
@@ -355,6 +361,9 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
     at.scale_log2 = 1.4426950408889634f / 8.0f;  // 1/sqrt(64) * log2(e)
     at.n_groups = B_r;
     at.q_rows_per_group = L;
+    ROCS_HIP(launch_vtrans(qkv + 2 * d, 3 * d, int64_t(L) * 3 * d, B_r, n_heads, L, vt, s), "encoder V^T");
+    at.vt = vt;
+    at.ldvt = vt_pad(L);
     ROCS_HIP(launch_attn(at, s), "encoder self-attention");
     ROCS_TRY(gemm_plain(att, d, rows, d, d, e.w_o, e.b_o, 0, Sin, d, tmp, d, s, "encoder out-proj"));
     ROCS_TRY(layer_norm_rows(rows, d, tmp, d, e.ln1_g, e.ln1_b, s));
@@ -384,7 +393,11 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
   return ROCS_OK;
 }
 
-size_t xattn_ws_bytes(int B_r, int B_c) { return align_up(attn_plan_ws_bytes(B_r, B_c), 256); }
+// plan (tiles per request) + V^T of the request and candidate value sets
+size_t xattn_plan_bytes(int B_r, int B_c) { return align_up(attn_plan_ws_bytes(B_r, B_c), 256); }
+size_t xattn_ws_bytes(int B_r, int B_c, int L, int d) {
+  return xattn_plan_bytes(B_r, B_c) + 2 * vt_bytes(B_r, L, d);
+}
 
 struct XattnPlan {
   int32_t* tiles = nullptr;
@@ -417,8 +430,9 @@ int xattn_check(const rocs_batch* batch, rocs_dtype dt, int32_t n_heads, int32_t
   return ROCS_OK;
 }
 
+// vt: V^T staging for B_r sequences (vt_bytes), or NULL to transpose inside the kernel
 int xattn_request_launch(int B_r, int H, int L, const void* q_r, int64_t ld_qr, const void* k_r, const void* v_r,
-                         int64_t ld_kv, float scale_log2, void* a_r, int64_t ld_ar, hipStream_t s) {
+                         int64_t ld_kv, float scale_log2, void* a_r, int64_t ld_ar, bf16* vt, hipStream_t s) {
   if (B_r == 0 || !q_r) return ROCS_OK;
   AttnArgs at{};
   at.n_heads = H;
@@ -434,13 +448,20 @@ int xattn_request_launch(int B_r, int H, int L, const void* q_r, int64_t ld_qr, 
   at.scale_log2 = scale_log2;
   at.n_groups = B_r;
   at.q_rows_per_group = 1;
+  if (vt) {
+    ROCS_HIP(launch_vtrans(reinterpret_cast<const bf16*>(v_r), ld_kv, int64_t(L) * ld_kv, B_r, H, L, vt, s),
+             "request V^T");
+    at.vt = vt;
+    at.ldvt = vt_pad(L);
+  }
   ROCS_HIP(launch_attn(at, s), "request cross-attention");
   return ROCS_OK;
 }
 
+// vt: V^T staging for the B_r value sets (vt_bytes); used with a plan (shared execution)
 int xattn_candidate_launch(int B_r, int B_c, const XattnPlan& plan, int H, int L, const void* q_c, int64_t ld_qc,
                            const void* k_c, const void* v_c, int64_t ld_kv, int64_t kv_group_stride, float scale_log2,
-                           void* a_c, int64_t ld_ac, hipStream_t s) {
+                           void* a_c, int64_t ld_ac, bf16* vt, hipStream_t s) {
   if (B_c == 0) return ROCS_OK;
   AttnArgs at{};
   at.n_heads = H;
@@ -461,6 +482,12 @@ int xattn_candidate_launch(int B_r, int B_c, const XattnPlan& plan, int H, int L
     at.n_tiles_dev = plan.n_tiles;
     at.perm = plan.perm;
     at.max_tiles = plan.max_tiles;
+    if (vt) {
+      ROCS_HIP(launch_vtrans(reinterpret_cast<const bf16*>(v_c), ld_kv, kv_group_stride, B_r, H, L, vt, s),
+               "candidate V^T");
+      at.vt = vt;
+      at.ldvt = vt_pad(L);
+    }
   } else {  // one group per candidate (dense-broadcast comparator)
     at.n_groups = B_c;
     at.q_rows_per_group = 1;
@@ -747,9 +774,9 @@ int rocs_dca_encode_kv(rocs_dtype dtype, int32_t B_r, int32_t L, int32_t d, int3
   return ok();
 }
 
-size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c) {
-  if (B_r < 0 || B_c < 0) return 0;
-  return xattn_ws_bytes(B_r, B_c);
+size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c, int32_t n_heads, int32_t L) {
+  if (B_r < 0 || B_c < 0 || n_heads <= 0 || L <= 0) return 0;
+  return xattn_ws_bytes(B_r, B_c, L, n_heads * 64);
 }
 
 int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim, int32_t L,
@@ -760,20 +787,25 @@ int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_hea
   ROCS_TRY(xattn_check(batch, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld_qc, k_r, v_r, k_c, v_c, ld_kv, a_r,
                        ld_ar, a_c, ld_ac, fn));
   const int B_r = batch->num_requests, B_c = batch->num_candidates;
-  const size_t need = xattn_ws_bytes(B_r, B_c);
-  if (B_c > 0 && (!workspace || ws_bytes < need))
+  const int d = n_heads * 64;
+  const size_t need = xattn_ws_bytes(B_r, B_c, L, d);
+  const bool work = B_c > 0 || (B_r > 0 && q_r);
+  if (work && (!workspace || ws_bytes < need))
     return fail(ROCS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
-  if (B_c > 0) ROCS_TRY(check_ptr(workspace, fn, "workspace"));
+  if (work) ROCS_TRY(check_ptr(workspace, fn, "workspace"));
   hipStream_t s = as_stream(stream);
   const float sl2 = scale_log2_of(scale);
-  ROCS_TRY(xattn_request_launch(B_r, n_heads, L, q_r, ld_qr, k_r, v_r, ld_kv, sl2, a_r, ld_ar, s));
+  char* ws = reinterpret_cast<char*>(workspace);
+  bf16* vt_r = work ? reinterpret_cast<bf16*>(ws + xattn_plan_bytes(B_r, B_c)) : nullptr;
+  bf16* vt_c = work ? reinterpret_cast<bf16*>(ws + xattn_plan_bytes(B_r, B_c) + vt_bytes(B_r, L, d)) : nullptr;
+  ROCS_TRY(xattn_request_launch(B_r, n_heads, L, q_r, ld_qr, k_r, v_r, ld_kv, sl2, a_r, ld_ar, vt_r, s));
   if (B_c > 0) {
     XattnPlan p;
     ROCS_HIP(launch_attn_plan(B_r, B_c, batch->offsets, batch->cand2req, workspace, &p.tiles, &p.n_tiles, &p.perm,
                               &p.max_tiles, s),
              fn);
     ROCS_TRY(xattn_candidate_launch(B_r, B_c, p, n_heads, L, q_c, ld_qc, k_c, v_c, ld_kv, int64_t(L) * ld_kv, sl2,
-                                    a_c, ld_ac, s));
+                                    a_c, ld_ac, vt_c, s));
   }
   return ok();
 }

@@ -29,6 +29,7 @@ __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chu
 // V^T tile: [64 dh][64 keys] bf16 in 8-byte units (16 per row), swizzled by dh.
 __device__ __forceinline__ int vt_off(int dh, int unit) { return dh * 16 + (unit ^ (dh & 15)); }
 
+template <bool VT>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   __shared__ uint4 sK[2][KC * 8];
   __shared__ uint2 sV[2][DH * 16];
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   const bf16* kbase = a.k + int64_t(group) * a.kv_group_stride + h * DH;
   const bf16* vbase = a.v + int64_t(group) * a.kv_group_stride + h * DH;
+  const bf16* vtbase = VT ? a.vt + (int64_t(group) * H + h) * DH * a.ldvt : nullptr;
   const int L = a.L;
   const int nslab = (L + KC - 1) / KC;
 
@@ -96,12 +98,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       const int id = tid + i * 256;
       const int key = id >> 3, c = id & 7;
       const int gk = slab * KC + key;
-      if (gk < L) {
-        rk[i] = *reinterpret_cast<const uint4*>(kbase + int64_t(gk) * a.ldkv + c * 8);
-        rv[i] = *reinterpret_cast<const uint4*>(vbase + int64_t(gk) * a.ldkv + c * 8);
+      rk[i] = gk < L ? *reinterpret_cast<const uint4*>(kbase + int64_t(gk) * a.ldkv + c * 8) : make_uint4(0, 0, 0, 0);
+      if constexpr (VT) {
+        // V^T row dh = id / 8, keys slab*64 + 8c .. +7 (padded with zeros up to ldvt)
+        rv[i] = *reinterpret_cast<const uint4*>(vtbase + int64_t(key) * a.ldvt + slab * KC + c * 8);
       } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
+        rv[i] = gk < L ? *reinterpret_cast<const uint4*>(vbase + int64_t(gk) * a.ldkv + c * 8) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -111,13 +113,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       const int id = tid + i * 256;
       const int key = id >> 3, c = id & 7;
       sK[buf][k_off(key, c)] = rk[i];
-      // transpose V: dh = c*8 + e, key -> unit key/4, lane-in-unit key%4
-      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rv[i]);
-      uint16_t* vt = reinterpret_cast<uint16_t*>(sV[buf]);
+      if constexpr (VT) {
+        // already transposed: row dh = id / 8 holds keys 8c .. 8c+7 = units 2c, 2c+1
+        sV[buf][vt_off(key, 2 * c)] = make_uint2(rv[i].x, rv[i].y);
+        sV[buf][vt_off(key, 2 * c + 1)] = make_uint2(rv[i].z, rv[i].w);
+      } else {
+        // transpose V: dh = c*8 + e, key -> unit key/4, lane-in-unit key%4
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rv[i]);
+        uint16_t* vt = reinterpret_cast<uint16_t*>(sV[buf]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dh = c * 8 + e;
-        vt[vt_off(dh, key >> 2) * 4 + (key & 3)] = e16[e];
+        for (int e = 0; e < 8; ++e) {
+          const int dh = c * 8 + e;
+          vt[vt_off(dh, key >> 2) * 4 + (key & 3)] = e16[e];
+        }
       }
     }
   };
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * c);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // v_exp_f32
     const float mc = m_new * c;
     float psum = 0.f;
     bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float p = exp2f(fmaf(s[kt][st * 8 + q], c, -mc));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + q], c, -mc));
           psum += p;
           pf[kt * 2 + st][q] = to_bf(p);
         }
@@ -223,6 +231,40 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
                    to_bf(o_acc[dt][4 * g + 2] * inv), to_bf(o_acc[dt][4 * g + 3] * inv)};
       *reinterpret_cast<bf16x4*>(o + dt * 32 + 8 * g + 4 * hl) = pk;
     }
+}
+
+// ----------------------------------------------------------------- V^T staging
+// The PV product takes V^T (keys contiguous per head dimension) as its A
+// operand.  Transposed once per call here (one 64-key block of one head of
+// one sequence per workgroup), every query tile then loads V^T rows with
+// 16-byte loads instead of transposing the same V in LDS again.
+__global__ __launch_bounds__(256) void vtrans_kernel(const bf16* __restrict__ v, int64_t ldv, int64_t gstride, int L,
+                                                     int H, int64_t Lp, bf16* __restrict__ vt) {
+  __shared__ uint16_t t[KC][DH + 2];  // [key][e]
+  const int kb = blockIdx.x, h = blockIdx.y, g = blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = tid + i * 256;
+    const int key = id >> 3, c = id & 7;
+    const int gk = kb * KC + key;
+    const uint4 u = gk < L ? *reinterpret_cast<const uint4*>(v + g * gstride + int64_t(gk) * ldv + h * DH + c * 8)
+                           : make_uint4(0, 0, 0, 0);
+    const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[key][c * 8 + e] = e16[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = tid + i * 256;
+    const int e = id >> 3, c = id & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = uint32_t(t[c * 8 + 2 * j][e]) | (uint32_t(t[c * 8 + 2 * j + 1][e]) << 16);
+    *reinterpret_cast<uint4*>(vt + ((int64_t(g) * H + h) * DH + e) * Lp + kb * KC + c * 8) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // ----------------------------------------------------------------- planning
@@ -370,7 +412,18 @@ hipError_t launch_attn_plan(int B_r, int B_c, const int32_t* offsets, const int3
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int tiles = a.q_rows_per_group > 0 ? a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ) : a.max_tiles;
   if (tiles <= 0 || a.n_heads <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  if (a.vt != nullptr)
+    hipLaunchKernelGGL(attn_kernel<true>, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_kernel<false>, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_vtrans(const bf16* v, int64_t ldv, int64_t gstride, int G, int H, int L, bf16* vt, hipStream_t s) {
+  if (G <= 0 || H <= 0 || L <= 0) return hipSuccess;
+  const int64_t Lp = vt_pad(L);
+  hipLaunchKernelGGL(vtrans_kernel, dim3(unsigned(Lp / KC), unsigned(H), unsigned(G)), dim3(256), 0, s, v, ldv,
+                     gstride, L, H, Lp, vt);
   return hipGetLastError();
 }
 

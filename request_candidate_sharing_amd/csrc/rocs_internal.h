@@ -108,8 +108,16 @@ struct AttnArgs {
   const int32_t* n_tiles_dev;
   const int32_t* perm;  // optional row permutation: logical row r is physical row perm[r]
   int max_tiles;
+  // optional V^T staging (launch_vtrans): vt[((g*H + h)*64 + e)*ldvt + key]; when
+  // set, v/ldkv are not read for values
+  const bf16* vt;
+  int64_t ldvt;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// V^T staging: vt[((g*H + h)*64 + e)*Lp + key] = v[g*gstride + key*ldv + h*64 + e] for
+// keys < L, 0 for L <= key < Lp = round_up(L, 64).
+hipError_t launch_vtrans(const bf16* v, int64_t ldv, int64_t gstride, int G, int H, int L, bf16* vt, hipStream_t s);
+inline int64_t vt_pad(int L) { return (int64_t(L) + 63) / 64 * 64; }
 int attn_tile_rows();
 
 // Builds per-request query tiles (and, without offsets, a counting sort of

@@ -121,7 +121,7 @@ _SIGS = {
     "rocs_dca_encode_kv_workspace_size": [c_int32, c_int32, c_int32, c_int32, c_int32],
     "rocs_dca_encode_kv": [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, c_int32, P, P, P, P,
                            c_size_t, P],
-    "rocs_dca_cross_attn_workspace_size": [c_int32, c_int32],
+    "rocs_dca_cross_attn_workspace_size": [c_int32, c_int32, c_int32, c_int32],
     "rocs_dca_cross_attn": [P, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, P, P, c_int64,
                             c_float, P, c_int64, P, c_int64, P, c_size_t, P],
     "rocs_broadcast_rows": [P, c_int64, P, c_int64, P, c_int64, P],
@@ -263,8 +263,8 @@ def rocs_dca_encode_kv(dtype, B_r, L, d, n_heads, ffn, seq, n_enc, enc, n_depths
     return _check(st) if check else st
 
 
-def rocs_dca_cross_attn_workspace_size(B_r, B_c) -> int:
-    return int(lib().rocs_dca_cross_attn_workspace_size(B_r, B_c))
+def rocs_dca_cross_attn_workspace_size(B_r, B_c, n_heads, L) -> int:
+    return int(lib().rocs_dca_cross_attn_workspace_size(B_r, B_c, n_heads, L))
 
 
 def rocs_dca_cross_attn(batch_, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld_qc, k_r, v_r, k_c, v_c, ld_kv, scale,

@@ -301,7 +301,7 @@ def xattn_case(counts, L, H, seed, shuffle=False):
     ac = torch.empty(max(Bc, 1), d, dtype=torch.bfloat16, device="cuda")
     off = None if shuffle else torch.as_tensor(bt["offsets"], device="cuda")
     c2r = torch.as_tensor(m[perm].astype(np.int32), device="cuda")
-    wsb = R.rocs_dca_cross_attn_workspace_size(B, Bc)
+    wsb = R.rocs_dca_cross_attn_workspace_size(B, Bc, H, L)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     R.rocs_dca_cross_attn(R.batch(B, Bc, off, c2r), R.ROCS_BF16, H, 64, L, qr_t, d, qc_t, d, kvt, kvt[:, d:],
                           kvt[:, 2 * d:], kvt[:, 3 * d:], 4 * d, 0.0, ar, d, ac, d, ws, wsb, R.cur_stream())
