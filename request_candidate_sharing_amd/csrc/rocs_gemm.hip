@@ -587,16 +587,56 @@ hipError_t launch_tiles(K kernel, int bm, int bn, int threads, const GemmArgs& a
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Tile height (256, 192 or 128 rows) for a one-workgroup-per-CU GEMM of M
+// rows and nt column tiles: fewest row-weighted rounds of workgroups, with
+// smaller tiles charged 15% per 64 rows for their extra operand traffic.
+int cand_tile_rows(int M, int nt) {
+  const int cus = device_cus();
+  int best = 256;
+  double best_cost = 0.0;
+  for (int bm : {256, 192, 128}) {
+    const long tiles = long((M + bm - 1) / bm) * nt;
+    const long rounds = (tiles + cus - 1) / cus;
+    const double cost = double(rounds) * bm * (1.0 + 0.15 * (256 - bm) / 64.0);
+    if (bm == 256 || cost < best_cost) {
+      best = bm;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (dt == F32) return launch_tiles(gemm_f32_kernel, 64, 64, 256, a, s);
   // All bf16 variants compute every element identically; the choice only
   // trades tile size against the number of workgroups.  Measured on the
   // candidate shapes (M = 73,704; K, N = 512/1024 both ways, interleaved
-  // medians): 256x256 tiles beat 128x128 ones (139 vs 164 us for N = 1024,
-  // 136 vs 137 us for N = 512): half the operand traffic from L2 per FLOP.
+  // medians): 256-wide tiles beat 128x128 ones (139 vs 164 us for N =
+  // 1024): half the operand traffic from L2 per FLOP.  One workgroup fits
+  // per CU, so the tile height is chosen to fill the last round of
+  // workgroups: for N = 512, 192-row tiles make 768 tiles (3 full rounds on
+  // 256 CUs) instead of 576 (2.25 rounds): 112 vs 134 us.
   if (a.M >= 2048) {
-    if (a.N > 128) return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);
+    if (a.N > 128) {
+      switch (cand_tile_rows(a.M, (a.N + 255) / 256)) {
+        case 192: return launch_tiles(gemm_bf16_big_kernel<192, 256, 2, 4>, 192, 256, 512, a, s);
+        case 128: return launch_tiles(gemm_bf16_big_kernel<128, 256, 2, 4>, 128, 256, 512, a, s);
+        default: return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);
+      }
+    }
     return launch_tiles(gemm_bf16_big_kernel<256, 128, 4, 2>, 256, 128, 512, a, s);
   }
   // Request batches (M <= a few hundred): the weights stream from HBM once
