@@ -9,16 +9,13 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The weight
 // fragment is the MFMA "A" operand and the activation fragment the "B"
 // operand, so each lane holds 4 consecutive output columns of one output row
-// per register group.  Two kernel families share the instruction, the LDS
-// layout rule and the accumulation order (64-wide K groups in ascending
-// order, four k16 steps per group with the k-sets of slab_mfma below):
-//   gemm_bf16_kernel      register-staged loads with element masking at
-//                         every edge (any M; used for request batches);
-//   gemm_bf16_big_kernel  global->LDS DMA (global_load_lds_dwordx4), no
-//                         register staging, zero page for K tails (large M;
-//                         candidate batches).
-// Every output element is therefore reduced in the same order whichever
-// kernel, tile shape or K-slab width computes it: results are bit-identical
+// per register group.  Every bf16 shape runs gemm_bf16_big_kernel: operands
+// move global->LDS by DMA (global_load_lds_dwordx4), with no register
+// staging and a zero page for K tails; only the tile shape changes between
+// request batches and candidate batches.  The accumulation order is fixed
+// (64-wide K groups in ascending order, four k16 steps per group with the
+// k-sets of slab_mfma below), so every output element is reduced in the
+// same order whichever tile shape computes it: results are bit-identical
 // across batch sizes and batch compositions.
 // Workgroup ids are remapped so that one XCD walks neighbouring tiles.
 #include "rocs_mfma.h"
@@ -26,15 +23,6 @@
 namespace rocs {
 
 namespace {
-
-__device__ __forceinline__ uint4 load_chunk(const bf16* p, int kc, int K) {
-  if (kc + 8 <= K) return *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-  for (int e = 0; e < 8; ++e)
-    if (kc + e < K) w[e >> 1] |= uint32_t(q[e]) << (16 * (e & 1));
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 __device__ __forceinline__ const bf16* weight_row(const GemmArgs& a, int n) {
   int s = 0, base = 0;
@@ -331,93 +319,6 @@ __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, 
 template <int FM, int FN>
 __device__ __forceinline__ void slab_mfma(const uint4* s, int xr0, int wr0, int hk, f32x16 (&acc)[FM][FN]) {
   mfma_steps<FM, FN, 4, 8, 8>(s, wr0, s, xr0, 0, hk, acc);
-}
-
-// ----------------------------------------------------------------- register-staged bf16 GEMM
-// WM x WN waves, BM x BN tile, BK = 64; operands staged global -> registers ->
-// LDS with element masking at the M, N and K edges; the next slab's global
-// loads are in flight while the current slab is multiplied.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int BK = 64, NT = WM * WN * 64;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int ACH = BM * 8 / NT, WCH = BN * 8 / NT;  // 16-byte chunks per thread per slab
-  static_assert(ACH * NT == BM * 8 && WCH * NT == BN * 8, "tile rows must divide among threads");
-  __shared__ uint4 smem[2][(BM + BN) * 8];
-
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = (a.M + BM - 1) / BM;
-  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
-  const int m0 = (logical / ntn) * BM;
-  const int n0 = (logical % ntn) * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  const bf16* A = reinterpret_cast<const bf16*>(a.A);
-  const bf16* aptr[ACH];
-  int aslot[ACH], achunk[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int id = tid + i * NT;
-    const int r = id >> 3, c = id & 7;
-    aptr[i] = A + int64_t(min(m0 + r, a.M - 1)) * a.lda + c * 8;
-    aslot[i] = slot<8>(r, c);
-    achunk[i] = c * 8;
-  }
-  const bf16* wptr[WCH];
-  int wslot[WCH], wchunk[WCH];
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int id = tid + i * NT;
-    const int r = id >> 3, c = id & 7;
-    wptr[i] = weight_row(a, min(n0 + r, a.N - 1)) + c * 8;
-    wslot[i] = slot<8>(BM + r, c);
-    wchunk[i] = c * 8;
-  }
-
-  f32x16 acc[FM][FN];
-  zero_acc(acc);
-
-  const int nk = (a.K + BK - 1) / BK;
-  uint4 ra[ACH], rw[WCH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) ra[i] = load_chunk(aptr[i], achunk[i], a.K);
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) rw[i] = load_chunk(wptr[i], wchunk[i], a.K);
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) smem[0][aslot[i]] = ra[i];
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) smem[0][wslot[i]] = rw[i];
-  __syncthreads();
-
-  const int xr0 = wm * WTM + (lane & 31);
-  const int wr0 = BM + wn * WTN + (lane & 31);
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    const bool more = kb + 1 < nk;
-    if (more) {
-      const int k0 = (kb + 1) * BK;
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) ra[i] = load_chunk(aptr[i] + k0, k0 + achunk[i], a.K);
-#pragma unroll
-      for (int i = 0; i < WCH; ++i) rw[i] = load_chunk(wptr[i] + k0, k0 + wchunk[i], a.K);
-    }
-    slab_mfma(smem[cur], xr0, wr0, lane >> 5, acc);
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) smem[cur ^ 1][aslot[i]] = ra[i];
-#pragma unroll
-      for (int i = 0; i < WCH; ++i) smem[cur ^ 1][wslot[i]] = rw[i];
-    }
-    __syncthreads();
-  }
-  static_assert(WM * WN * stage_floats<FN>() * 4 <= int(sizeof(smem)), "epilogue stage exceeds LDS");
-  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
-               reinterpret_cast<float*>(&smem[0][0]) + wave * stage_floats<FN>());
 }
 
 // ----------------------------------------------------------------- DMA-staged bf16 GEMM
