@@ -14,7 +14,7 @@
 // staging and a zero page for K tails; only the tile shape changes between
 // request batches and candidate batches.  The accumulation order is fixed
 // (64-wide K groups in ascending order, four k16 steps per group with the
-// k-sets of slab_mfma below), so every output element is reduced in the
+// k-sets of kchunk in rocs_mfma.h), so every output element is reduced in the
 // same order whichever tile shape computes it: results are bit-identical
 // across batch sizes and batch compositions.
 // Workgroup ids are remapped so that one XCD walks neighbouring tiles.
@@ -109,10 +109,13 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
   }
 }
 
-// Per-wave LDS stage of the transposing epilogue: 32 rows of FN*32 fp32
-// accumulators, rows padded by 16 bytes (conflict-free both ways).
+// Per-wave LDS stage of the transposing epilogue: 32 rows of up to 64 fp32
+// accumulators (two 32x32 blocks), rows padded by 16 bytes (conflict-free
+// both ways).  Wider wave tiles go through it two blocks at a time.
 template <int FN>
-constexpr int stage_pitch() { return FN * 32 + 4; }
+constexpr int stage_blocks() { return FN > 2 ? 2 : FN; }
+template <int FN>
+constexpr int stage_pitch() { return stage_blocks<FN>() * 32 + 4; }
 template <int FN>
 constexpr int stage_floats() { return 32 * stage_pitch<FN>(); }
 
@@ -121,15 +124,17 @@ constexpr int stage_floats() { return 32 * stage_pitch<FN>(); }
 // in registers 4g..4g+3.  Stored directly, every instruction would touch 32
 // rows (half the achievable write bandwidth), so interior tiles pass each
 // block-row of fp32 accumulators through the wave's LDS stage and come back
-// row-contiguous (FN*8 lanes per row, 4 columns each).  All loads of a
-// block-row (map entries, Z rows, residual) are issued before its
-// arithmetic and stores.  The arithmetic is the edge path's: acc + Z + bias,
-// act, + residual, one rounding.
+// row-contiguous (JW*8 lanes per row, 4 columns each), JW column blocks at a
+// time.  All loads of a pass (map entries, Z rows, residual) are issued
+// before its arithmetic and stores.  The arithmetic is the edge path's:
+// acc + Z + bias, act, + residual, one rounding.
 template <int FM, int FN>
 __device__ __forceinline__ void store_blocks_staged(const GemmArgs& a, int mb, int nb, int lane,
                                                     f32x16 (&acc)[FM][FN], float* stage) {
+  constexpr int JW = stage_blocks<FN>();
+  static_assert(FN % JW == 0, "column blocks must pair up");
   constexpr int P = stage_pitch<FN>();
-  constexpr int LPR = FN * 8;     // lanes per row
+  constexpr int LPR = JW * 8;     // lanes per row
   constexpr int RPI = 64 / LPR;   // rows per pass
   constexpr int NP = 32 / RPI;    // passes per block-row
   const int hk = lane >> 5;
@@ -138,67 +143,73 @@ __device__ __forceinline__ void store_blocks_staged(const GemmArgs& a, int mb, i
   const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
   bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
   const int rl = lane / LPR;
-  const int n = nb + (lane % LPR) * 4;
-  float bv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (bias != nullptr) {
-    const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + n);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bv[e] = to_f(bb[e]);
-  }
+  for (int jg = 0; jg < FN / JW; ++jg) {
+    const int n = nb + jg * JW * 32 + (lane % LPR) * 4;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+      const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + n);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int mrow0 = mb + i * 32;
-    // map entries and residuals of this lane's NP rows, issued before the LDS round trip
-    int zrow[NP];
-    bf16x4 rr[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int m = min(mrow0 + p * RPI + rl, a.M - 1);
-      zrow[p] = (z != nullptr && a.zmap != nullptr) ? a.zmap[m] : m;
-      if (res != nullptr) rr[p] = *reinterpret_cast<const bf16x4*>(res + int64_t(m) * a.ldres + n);
+      for (int e = 0; e < 4; ++e) bv[e] = to_f(bb[e]);
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + j * 32 + 8 * g + 4 * hk) =
-            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-    __builtin_amdgcn_wave_barrier();
-    float4 zz[NP];
-    if (z != nullptr) {
+    for (int i = 0; i < FM; ++i) {
+      const int mrow0 = mb + i * 32;
+      // map entries and residuals of this lane's NP rows, issued before the LDS round trip
+      int zrow[NP];
+      bf16x4 rr[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int zr = (unsigned)zrow[p] < (unsigned)a.zrows ? zrow[p] : 0;
-        zz[p] = *reinterpret_cast<const float4*>(z + int64_t(zr) * a.ldz + n);
+        const int m = min(mrow0 + p * RPI + rl, a.M - 1);
+        zrow[p] = (z != nullptr && a.zmap != nullptr) ? a.zmap[m] : m;
+        if (res != nullptr) rr[p] = *reinterpret_cast<const bf16x4*>(res + int64_t(m) * a.ldres + n);
       }
-    }
-    f32x4 sv[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
-    __builtin_amdgcn_wave_barrier();
+      for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int m = mrow0 + p * RPI + rl;
-      float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& c = acc[i][jg * JW + jj];
+          *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
+              f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+        }
+      __builtin_amdgcn_wave_barrier();
+      float4 zz[NP];
       if (z != nullptr) {
-        const bool bad = (unsigned)zrow[p] >= (unsigned)a.zrows;
-        v[0] = bad ? nan_f() : v[0] + zz[p].x;
-        v[1] = bad ? nan_f() : v[1] + zz[p].y;
-        v[2] = bad ? nan_f() : v[2] + zz[p].z;
-        v[3] = bad ? nan_f() : v[3] + zz[p].w;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int zr = (unsigned)zrow[p] < (unsigned)a.zrows ? zrow[p] : 0;
+          zz[p] = *reinterpret_cast<const float4*>(z + int64_t(zr) * a.ldz + n);
+        }
       }
-      if (bias != nullptr)
+      f32x4 sv[NP];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += bv[e];
-      if (a.act == 1)
+      for (int p = 0; p < NP; ++p)
+        sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
-      if (res != nullptr)
+      for (int p = 0; p < NP; ++p) {
+        const int m = mrow0 + p * RPI + rl;
+        float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
+        if (z != nullptr) {
+          const bool bad = (unsigned)zrow[p] >= (unsigned)a.zrows;
+          v[0] = bad ? nan_f() : v[0] + zz[p].x;
+          v[1] = bad ? nan_f() : v[1] + zz[p].y;
+          v[2] = bad ? nan_f() : v[2] + zz[p].z;
+          v[3] = bad ? nan_f() : v[3] + zz[p].w;
+        }
+        if (bias != nullptr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
-      if (m < a.M) {
-        bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
-        *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + n) = pk;
+          for (int e = 0; e < 4; ++e) v[e] += bv[e];
+        if (a.act == 1)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
+        if (res != nullptr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
+        if (m < a.M) {
+          bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
+          *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + n) = pk;
+        }
       }
     }
   }
@@ -314,13 +325,6 @@ __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, 
   }
 }
 
-// One 64-wide K slab from the LDS tile s: weights (A operand) at rows wr0,
-// activations (B operand) at rows xr0, four k16 steps in the library's K order.
-template <int FM, int FN>
-__device__ __forceinline__ void slab_mfma(const uint4* s, int xr0, int wr0, int hk, f32x16 (&acc)[FM][FN]) {
-  mfma_steps<FM, FN, 4, 8, 8>(s, wr0, s, xr0, 0, hk, acc);
-}
-
 // ----------------------------------------------------------------- DMA-staged bf16 GEMM
 // For the candidate-batch GEMMs (M = B_c in the tens of thousands).  A
 // BM x BN tile per workgroup of WM x WN waves; each wave owns a
@@ -394,11 +398,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
     else
       src[j] = weight_row(a, min(n0 + r - BM, a.N - 1)) + chunk * 8;
   }
+  // The zero page's address comes from the GOT.  Loaded inside the loop, that
+  // scalar load (out of order with LDS reads on the same counter) would turn
+  // every fragment wait into a full lgkmcnt(0); pinned in SGPRs here, it is
+  // loaded once.
+  const void* zero = g_zero_page;
+  asm volatile("" : "+s"(zero));
   auto issue = [&](int k0, int st) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const void* p = (k0 + kofs[j] < a.K) ? static_cast<const void*>(src[j] + k0)
-                                          : static_cast<const void*>(g_zero_page);
+      const void* p = (k0 + kofs[j] < a.K) ? static_cast<const void*>(src[j] + k0) : zero;
       __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(&smem[st][(wave * PER + j) * 64]), 16, 0, 0);
     }
   };
@@ -413,16 +422,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
 
   const int xr0 = wm * WTM + (lane & 31);
   const int wr0 = BM + wn * WTN + (lane & 31);
+  Frags<FM, FN> fr;
   for (int kb = 0; kb < nk; ++kb) {
     // Slab kb has landed once at most min(NS-2, nk-1-kb) newer slabs (PER
     // instructions each, returned in order) are still outstanding.
     wait_slabs<PER, NS - 2>(min(NS - 2, nk - 1 - kb));
     // every wave's part of slab kb is in LDS, and every wave is done with
-    // slab kb-1, whose buffer the next issue refills
+    // slab kb-1 (its last step's fragments are in registers), whose buffer
+    // the next issue refills
     __syncthreads();
     if (kb + NS - 1 < nk) issue((kb + NS - 1) * BK, (kb + NS - 1) % NS);
-    slab_mfma(smem[kb % NS], xr0, wr0, lane >> 5, acc);
+    const uint4* sl = smem[kb % NS];
+    mfma_slab_carry<FM, FN, CPR, CPR>(fr, kb > 0, sl, wr0, sl, xr0, lane >> 5, acc);
   }
+  if (nk > 0) mfma_frags(fr, 1, acc);
   wait_vmcnt<0>();
   __syncthreads();  // the epilogue reuses the ring as its staging buffer
   if constexpr (STG) {

@@ -85,4 +85,60 @@ __device__ __forceinline__ void mfma_steps(const uint4* sa, int ar0, const uint4
   }
 }
 
+// Fragment registers of one wave, double-buffered by k16 step parity.
+template <int FM, int FN>
+struct Frags {
+  bf16x8 a[2][FN], b[2][FM];
+};
+
+template <int FM, int FN, int CPRA, int CPRB>
+__device__ __forceinline__ void load_frags(Frags<FM, FN>& f, int buf, const uint4* sa, int ar0, const uint4* sb,
+                                           int br0, int ch) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) f.a[buf][j] = __builtin_bit_cast(bf16x8, sa[slot<CPRA>(ar0 + j * 32, ch)]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) f.b[buf][i] = __builtin_bit_cast(bf16x8, sb[slot<CPRB>(br0 + i * 32, ch)]);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_frags(const Frags<FM, FN>& f, int buf, f32x16 (&acc)[FM][FN], int from = 0) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      if (i * FN + j >= from)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][j], f.b[buf][i], acc[i][j], 0, 0, 0);
+}
+
+// One 64-wide K slab (four k16 steps, library K order) with the last step
+// carried over: its fragments stay in buffer 1 and are multiplied by the
+// next call (carry = true) right after that call has requested its slab's
+// first fragments, so those MFMAs cover the LDS latency at the slab start
+// (behind the slab barrier).  The caller multiplies the final carried step
+// after the last slab (mfma_frags(f, 1, acc)).
+//
+// In a loop that also issues LDS DMA, the compiler waits for fragment reads
+// with lgkmcnt(0) (it takes the counter to be out of order), so a wait
+// covers every read issued so far.  Each step therefore issues its first
+// MFMA (whose wait then covers only that step's own fragments) before it
+// requests the next step's fragments, which the remaining MFMAs cover.
+// The accumulation order is unchanged.
+template <int FM, int FN, int CPRA, int CPRB>
+__device__ __forceinline__ void mfma_slab_carry(Frags<FM, FN>& f, bool carry, const uint4* sa, int ar0,
+                                                const uint4* sb, int br0, int hk, f32x16 (&acc)[FM][FN]) {
+  load_frags<FM, FN, CPRA, CPRB>(f, 0, sa, ar0, sb, br0, kchunk(0, hk));
+  __builtin_amdgcn_sched_barrier(0);
+  if (carry) mfma_frags(f, 1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 3; ++ks) {
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks & 1][0], f.b[ks & 1][0], acc[0][0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<FM, FN, CPRA, CPRB>(f, (ks + 1) & 1, sa, ar0, sb, br0, kchunk(ks + 1, hk));
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_frags(f, ks & 1, acc, 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 }  // namespace rocs
