@@ -24,15 +24,38 @@ namespace rocs {
 
 namespace {
 
+// Weight rows of the (up to four) segments.  The segment table is copied
+// out of the argument struct through an opaque asm into SGPRs and selected
+// as plain values: selected as struct fields or argument memory, the choice
+// becomes a per-lane indexed load (from argument memory, or from a private
+// copy of the table that the compiler then places in LDS).
+struct WeightSegs {
+  const bf16 *w0, *w1, *w2, *w3;
+  int e0, e1, e2;
+};
+
+__device__ __forceinline__ WeightSegs weight_segs(const GemmArgs& a) {
+  const bf16* x0 = reinterpret_cast<const bf16*>(a.W[0]);
+  const bf16* x1 = reinterpret_cast<const bf16*>(a.nseg > 1 ? a.W[1] : a.W[0]);
+  const bf16* x2 = reinterpret_cast<const bf16*>(a.nseg > 2 ? a.W[2] : a.W[0]);
+  const bf16* x3 = reinterpret_cast<const bf16*>(a.nseg > 3 ? a.W[3] : a.W[0]);
+  int y0 = a.nseg > 1 ? a.seg_end[0] : 0x7fffffff;
+  int y1 = a.nseg > 2 ? a.seg_end[1] : 0x7fffffff;
+  int y2 = a.nseg > 3 ? a.seg_end[2] : 0x7fffffff;
+  asm volatile("" : "+s"(x0), "+s"(x1), "+s"(x2), "+s"(x3), "+s"(y0), "+s"(y1), "+s"(y2));
+  return WeightSegs{x0, x1, x2, x3, y0, y1, y2};
+}
+
+__device__ __forceinline__ const bf16* weight_row(const bf16* w0, const bf16* w1, const bf16* w2, const bf16* w3,
+                                                  int e0, int e1, int e2, int64_t ldw, int n) {
+  const bf16* p = n >= e2 ? w3 : n >= e1 ? w2 : n >= e0 ? w1 : w0;
+  const int base = n >= e2 ? e2 : n >= e1 ? e1 : n >= e0 ? e0 : 0;
+  return p + int64_t(n - base) * ldw;
+}
+
 __device__ __forceinline__ const bf16* weight_row(const GemmArgs& a, int n) {
-  int s = 0, base = 0;
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (s + 1 < a.nseg && n >= a.seg_end[s]) {
-      base = a.seg_end[s];
-      ++s;
-    }
-  return reinterpret_cast<const bf16*>(a.W[s]) + int64_t(n - base) * a.ldw;
+  const WeightSegs t = weight_segs(a);
+  return weight_row(t.w0, t.w1, t.w2, t.w3, t.e0, t.e1, t.e2, a.ldw, n);
 }
 
 template <typename T>
@@ -109,6 +132,27 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
   }
 }
 
+// Epilogue of one element (m, c), same arithmetic as epilogue4.
+template <typename T>
+__device__ __forceinline__ void epilogue1(const GemmArgs& a, int m, int c, float v) {
+  if (m >= a.M || c >= a.N) return;
+  if (c < a.n_split) {
+    if (a.z != nullptr) {
+      const int zrow = a.zmap != nullptr ? a.zmap[m] : m;
+      v = (unsigned)zrow >= (unsigned)a.zrows ? nan_f() : v + a.z[int64_t(zrow) * a.ldz + c];
+    }
+    if (a.bias != nullptr) v += load_elem<T>(a.bias, c);
+    if (a.act == 1) v = fmaxf(v, 0.0f);
+    if (a.res != nullptr) v += load_elem<T>(a.res, int64_t(m) * a.ldres + c);
+    if (a.out0_f32)
+      reinterpret_cast<float*>(a.out0)[int64_t(m) * a.ld0 + c] = v;
+    else
+      reinterpret_cast<T*>(a.out0)[int64_t(m) * a.ld0 + c] = from_f<T>(v);
+  } else if (a.out1 != nullptr) {
+    a.out1[int64_t(m) * a.ld1 + (c - a.n_split)] = v;
+  }
+}
+
 // Per-wave LDS stage of the transposing epilogue: 32 rows of up to 64 fp32
 // accumulators (two 32x32 blocks), rows padded by 16 bytes (conflict-free
 // both ways).  Wider wave tiles go through it two blocks at a time.
@@ -119,18 +163,31 @@ constexpr int stage_pitch() { return stage_blocks<FN>() * 32 + 4; }
 template <int FN>
 constexpr int stage_floats() { return 32 * stage_pitch<FN>(); }
 
-// Writes one wave's 32x32 blocks through the epilogue.  Block (i, j): lane
-// holds row mb + 32i + lane%32 and columns nb + 32j + 8g + 4*(lane/32) + 0..3
-// in registers 4g..4g+3.  Stored directly, every instruction would touch 32
-// rows (half the achievable write bandwidth), so interior tiles pass each
-// block-row of fp32 accumulators through the wave's LDS stage and come back
+// Epilogue variants.  EPI_ANY tests every optional term at run time; the
+// others are fixed at compile time for the candidate GEMMs of the layer
+// stacks (request contribution gathered through the map, bias, then ReLU or
+// a residual), with 32-bit row offsets (launch_gemm checks the ranges).
+enum : int {
+  EPI_ANY = 0,
+  EPI_Z = 1,     // z with zmap
+  EPI_BIAS = 2,
+  EPI_RELU = 4,
+  EPI_RES = 8,
+};
+
+// Writes one 32-row block-row of a wave's tile through the epilogue.  Block
+// j: lane holds row mrow0 + lane%32 and columns nb + 32j + 8g +
+// 4*(lane/32) + 0..3 in registers 4g..4g+3.  Stored directly, every
+// instruction would touch 32 rows (half the achievable write bandwidth), so
+// interior blocks pass through the wave's LDS stage and come back
 // row-contiguous (JW*8 lanes per row, 4 columns each), JW column blocks at a
 // time.  All loads of a pass (map entries, Z rows, residual) are issued
 // before its arithmetic and stores.  The arithmetic is the edge path's:
 // acc + Z + bias, act, + residual, one rounding.
-template <int FM, int FN>
-__device__ __forceinline__ void store_blocks_staged(const GemmArgs& a, int mb, int nb, int lane,
-                                                    f32x16 (&acc)[FM][FN], float* stage) {
+template <int FN, int EPI = EPI_ANY>
+__device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, int nb, int lane,
+                                                 const f32x16 (&row)[FN], float* stage) {
+  constexpr bool ANY = EPI == EPI_ANY;
   constexpr int JW = stage_blocks<FN>();
   static_assert(FN % JW == 0, "column blocks must pair up");
   constexpr int P = stage_pitch<FN>();
@@ -142,186 +199,143 @@ __device__ __forceinline__ void store_blocks_staged(const GemmArgs& a, int mb, i
   const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
   const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
   bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
+  const bool has_z = ANY ? z != nullptr : (EPI & EPI_Z) != 0;
+  const bool has_map = ANY ? a.zmap != nullptr : (EPI & EPI_Z) != 0;
+  const bool has_bias = ANY ? bias != nullptr : (EPI & EPI_BIAS) != 0;
+  const bool relu = ANY ? a.act == 1 : (EPI & EPI_RELU) != 0;
+  const bool has_res = ANY ? res != nullptr : (EPI & EPI_RES) != 0;
   const int rl = lane / LPR;
 #pragma unroll
   for (int jg = 0; jg < FN / JW; ++jg) {
     const int n = nb + jg * JW * 32 + (lane % LPR) * 4;
+    // map entries and residuals of this lane's NP rows, issued before the LDS round trip
+    int zrow[NP];
+    bf16x4 rr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = min(mrow0 + p * RPI + rl, a.M - 1);
+      zrow[p] = (has_z && has_map) ? a.zmap[m] : m;
+      if (has_res) {
+        const bf16* rp = ANY ? res + int64_t(m) * a.ldres + n : res + (uint32_t(m) * uint32_t(a.ldres) + n);
+        rr[p] = *reinterpret_cast<const bf16x4*>(rp);
+      }
+    }
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr) {
+    if (has_bias) {
       const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + n);
 #pragma unroll
       for (int e = 0; e < 4; ++e) bv[e] = to_f(bb[e]);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int mrow0 = mb + i * 32;
-      // map entries and residuals of this lane's NP rows, issued before the LDS round trip
-      int zrow[NP];
-      bf16x4 rr[NP];
+    for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& c = row[jg * JW + jj];
+        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
+            f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+      }
+    __builtin_amdgcn_wave_barrier();
+    float4 zz[NP];
+    bool bad[NP];
+    if (has_z) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int m = min(mrow0 + p * RPI + rl, a.M - 1);
-        zrow[p] = (z != nullptr && a.zmap != nullptr) ? a.zmap[m] : m;
-        if (res != nullptr) rr[p] = *reinterpret_cast<const bf16x4*>(res + int64_t(m) * a.ldres + n);
+        bad[p] = (unsigned)zrow[p] >= (unsigned)a.zrows;
+        const int zr = bad[p] ? 0 : zrow[p];
+        const float* zp = ANY ? z + int64_t(zr) * a.ldz + n : z + (uint32_t(zr) * uint32_t(a.ldz) + n);
+        zz[p] = *reinterpret_cast<const float4*>(zp);
       }
+    }
+    f32x4 sv[NP];
 #pragma unroll
-      for (int jj = 0; jj < JW; ++jj)
+    for (int p = 0; p < NP; ++p)
+      sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& c = acc[i][jg * JW + jj];
-          *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
-              f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
-        }
-      __builtin_amdgcn_wave_barrier();
-      float4 zz[NP];
-      if (z != nullptr) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int zr = (unsigned)zrow[p] < (unsigned)a.zrows ? zrow[p] : 0;
-          zz[p] = *reinterpret_cast<const float4*>(z + int64_t(zr) * a.ldz + n);
-        }
+    for (int p = 0; p < NP; ++p) {
+      const int m = mrow0 + p * RPI + rl;
+      float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
+      if (has_z) {
+        v[0] = bad[p] ? nan_f() : v[0] + zz[p].x;
+        v[1] = bad[p] ? nan_f() : v[1] + zz[p].y;
+        v[2] = bad[p] ? nan_f() : v[2] + zz[p].z;
+        v[3] = bad[p] ? nan_f() : v[3] + zz[p].w;
       }
-      f32x4 sv[NP];
+      if (has_bias)
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
-      __builtin_amdgcn_wave_barrier();
+        for (int e = 0; e < 4; ++e) v[e] += bv[e];
+      if (relu)
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int m = mrow0 + p * RPI + rl;
-        float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
-        if (z != nullptr) {
-          const bool bad = (unsigned)zrow[p] >= (unsigned)a.zrows;
-          v[0] = bad ? nan_f() : v[0] + zz[p].x;
-          v[1] = bad ? nan_f() : v[1] + zz[p].y;
-          v[2] = bad ? nan_f() : v[2] + zz[p].z;
-          v[3] = bad ? nan_f() : v[3] + zz[p].w;
-        }
-        if (bias != nullptr)
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
+      if (has_res)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += bv[e];
-        if (a.act == 1)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
-        if (res != nullptr)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
-        if (m < a.M) {
-          bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
-          *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + n) = pk;
-        }
+        for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
+      if (m < a.M) {
+        bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
+        bf16* op = ANY ? out + int64_t(m) * a.ld0 + n : out + (uint32_t(m) * uint32_t(a.ld0) + n);
+        *reinterpret_cast<bf16x4*>(op) = pk;
       }
     }
   }
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, f32x16 (&acc)[FM][FN],
-                                             float* stage = nullptr) {
+// Edge block-rows (N tail, the split between the two outputs, fp32 output):
+// the block-row goes through the LDS stage too, then one element per lane
+// at a time through epilogue1 (no register array is indexed at run time).
+template <int FN>
+__device__ __forceinline__ void store_row_edge(const GemmArgs& a, int mrow0, int nb, int lane,
+                                               const f32x16 (&row)[FN], float* stage) {
+  constexpr int JW = stage_blocks<FN>();
+  constexpr int P = stage_pitch<FN>();
+  constexpr int W = JW * 32;
   const int hk = lane >> 5;
-  const bool interior = (nb + FN * 32 <= a.N) && (nb + FN * 32 <= a.n_split) && !a.out0_f32;
-  if (interior && stage != nullptr) {
-    store_blocks_staged(a, mb, nb, lane, acc, stage);
-    return;
-  }
-  if (interior) {
-    const float* __restrict__ z = a.z;
-    const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
-    const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
-    bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = mb + i * 32 + (lane & 31);
-      const bool mok = m < a.M;
-      const int mr = mok ? m : a.M - 1;
-      int zrow = mr;
-      bool bad = false;
-      if (z != nullptr && a.zmap != nullptr) {
-        zrow = a.zmap[mr];
-        bad = (unsigned)zrow >= (unsigned)a.zrows;
-        zrow = bad ? 0 : zrow;
-      }
-      float v[FN][4][4];
+  for (int jg = 0; jg < FN / JW; ++jg) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[j][g][e] = acc[i][j][4 * g + e];
-      if (z != nullptr) {
-        float4 zz[FN][4];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            zz[j][g] = *reinterpret_cast<const float4*>(z + int64_t(zrow) * a.ldz + nb + j * 32 + 8 * g + 4 * hk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            v[j][g][0] = bad ? nan_f() : v[j][g][0] + zz[j][g].x;
-            v[j][g][1] = bad ? nan_f() : v[j][g][1] + zz[j][g].y;
-            v[j][g][2] = bad ? nan_f() : v[j][g][2] + zz[j][g].z;
-            v[j][g][3] = bad ? nan_f() : v[j][g][3] + zz[j][g].w;
-          }
-      }
-      if (bias != nullptr) {
-        bf16x4 bb[FN][4];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) bb[j][g] = *reinterpret_cast<const bf16x4*>(bias + nb + j * 32 + 8 * g + 4 * hk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[j][g][e] += to_f(bb[j][g][e]);
-      }
-      if (a.act == 1)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[j][g][e] = fmaxf(v[j][g][e], 0.f);
-      if (res != nullptr) {
-        bf16x4 rr[FN][4];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            rr[j][g] = *reinterpret_cast<const bf16x4*>(res + int64_t(mr) * a.ldres + nb + j * 32 + 8 * g + 4 * hk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[j][g][e] += to_f(rr[j][g][e]);
-      }
-      if (mok) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 pk = {to_bf(v[j][g][0]), to_bf(v[j][g][1]), to_bf(v[j][g][2]), to_bf(v[j][g][3])};
-            *reinterpret_cast<bf16x4*>(out + int64_t(m) * a.ld0 + nb + j * 32 + 8 * g + 4 * hk) = pk;
-          }
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = mb + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = nb + j * 32 + 8 * g + 4 * hk;
-        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        epilogue4<bf16>(a, m, n, v);
+        const f32x16& c = row[jg * JW + jj];
+        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
+            f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
       }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < 32 * W; e += 64) {
+      const int r = e / W, c = e % W;
+      epilogue1<bf16>(a, mrow0 + r, nb + jg * W + c, stage[r * P + c]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int FN, int EPI>
+__device__ __forceinline__ void store_row(const GemmArgs& a, int mrow0, int nb, int lane, const f32x16 (&row)[FN],
+                                          float* stage) {
+  const bool interior = (nb + FN * 32 <= a.N) && (nb + FN * 32 <= a.n_split) && !a.out0_f32;
+  if (interior)
+    store_row_staged<FN, EPI>(a, mrow0, nb, lane, row, stage);
+  else
+    store_row_edge(a, mrow0, nb, lane, row, stage);
+}
+
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void store_blocks_as(const GemmArgs& a, int mb, int nb, int lane,
+                                                const f32x16 (&acc)[FM][FN], float* stage) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) store_row<FN, EPI>(a, mb + i * 32, nb, lane, acc[i], stage);
+}
+
+// The epilogue variant is uniform per launch: one switch, then straight-line
+// code without per-element feature tests.
+template <int FM, int FN>
+__device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, const f32x16 (&acc)[FM][FN],
+                                             float* stage) {
+  switch (a.epi) {
+    case EPI_Z | EPI_BIAS | EPI_RELU: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RELU>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_BIAS | EPI_RES: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RES>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_RELU: store_blocks_as<EPI_Z | EPI_RELU>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_RES: store_blocks_as<EPI_Z | EPI_RES>(a, mb, nb, lane, acc, stage); break;
+    default: store_blocks_as<EPI_ANY>(a, mb, nb, lane, acc, stage); break;
   }
 }
 
@@ -364,8 +378,10 @@ __device__ __forceinline__ void wait_slabs(int newer) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS = 2, bool STG = true>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
+// One BM x BN output tile at (m0, n0) on a workgroup of WM x WN waves, with
+// the ring (NS slots of BM + BN rows of one 64-wide slab) at smem.
+template <int BM, int BN, int WM, int WN, int NS>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uint4* smem) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -376,16 +392,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   static_assert(RB % NW == 0, "row blocks must divide among waves");
   constexpr int PER = RB / NW;
   static_assert(NS >= 2 && PER * (NS - 2) < 64, "ring depth");
-  __shared__ uint4 smem[NS][(BM + BN) * CPR];
-
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = (a.M + BM - 1) / BM;
-  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
-  const int m0 = (logical / ntn) * BM;
-  const int n0 = (logical % ntn) * BN;
+  constexpr int SLAB = (BM + BN) * CPR;     // uint4 per ring slot
+  static_assert(NW * stage_floats<FN>() * 4 <= NS * SLAB * 16, "epilogue stage exceeds the ring");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
+  // The zero page's address comes from the GOT.  Loaded inside the loop, that
+  // scalar load (out of order with LDS reads on the same counter) would turn
+  // every fragment wait into a full lgkmcnt(0); pinned in SGPRs here, it is
+  // loaded once.  The weight segment table is pinned the same way, outside
+  // the lane-dependent row selection below.
+  const void* zero = g_zero_page;
+  asm volatile("" : "+s"(zero));
+  const WeightSegs ws = weight_segs(a);
   const bf16* src[PER];
   int kofs[PER];
 #pragma unroll
@@ -396,19 +415,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
     if (r < BM)
       src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
     else
-      src[j] = weight_row(a, min(n0 + r - BM, a.N - 1)) + chunk * 8;
+      src[j] = weight_row(ws.w0, ws.w1, ws.w2, ws.w3, ws.e0, ws.e1, ws.e2, a.ldw, min(n0 + r - BM, a.N - 1)) +
+               chunk * 8;
   }
-  // The zero page's address comes from the GOT.  Loaded inside the loop, that
-  // scalar load (out of order with LDS reads on the same counter) would turn
-  // every fragment wait into a full lgkmcnt(0); pinned in SGPRs here, it is
-  // loaded once.
-  const void* zero = g_zero_page;
-  asm volatile("" : "+s"(zero));
   auto issue = [&](int k0, int st) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const void* p = (k0 + kofs[j] < a.K) ? static_cast<const void*>(src[j] + k0) : zero;
-      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(&smem[st][(wave * PER + j) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(smem + st * SLAB + (wave * PER + j) * 64), 16, 0, 0);
     }
   };
 
@@ -432,19 +446,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
     // the next issue refills
     __syncthreads();
     if (kb + NS - 1 < nk) issue((kb + NS - 1) * BK, (kb + NS - 1) % NS);
-    const uint4* sl = smem[kb % NS];
+    const uint4* sl = smem + (kb % NS) * SLAB;
     mfma_slab_carry<FM, FN, CPR, CPR>(fr, kb > 0, sl, wr0, sl, xr0, lane >> 5, acc);
   }
   if (nk > 0) mfma_frags(fr, 1, acc);
   wait_vmcnt<0>();
   __syncthreads();  // the epilogue reuses the ring as its staging buffer
-  if constexpr (STG) {
-    static_assert(NW * stage_floats<FN>() * 4 <= int(sizeof(smem)), "epilogue stage exceeds LDS");
-    store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
-                 reinterpret_cast<float*>(&smem[0][0]) + wave * stage_floats<FN>());
-  } else {
-    store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
-  }
+  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
+               reinterpret_cast<float*>(smem) + wave * stage_floats<FN>());
+}
+
+// One tile per workgroup, tiles in XCD-aware order.
+template <int BM, int BN, int WM, int WN, int NS = 2>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
+  __shared__ uint4 smem[NS * (BM + BN) * 8];
+  const int ntn = (a.N + BN - 1) / BN;
+  const int ntm = (a.M + BM - 1) / BM;
+  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
+  gemm_tile<BM, BN, WM, WN, NS>(a, (logical / ntn) * BM, (logical % ntn) * BN, smem);
 }
 
 // fp32 path: LDS-tiled SIMT GEMM, 64 x 64 tile, each thread 4 x 4 outputs,
@@ -532,7 +551,28 @@ int cand_tile_rows(int M, int nt) {
   return best;
 }
 
-hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s) {
+// Epilogue variant of a launch: one of the specialised ones when the terms
+// match and every offset fits 32 bits, else EPI_ANY.
+int epilogue_variant(const GemmArgs& a) {
+  if (a.z == nullptr || a.zmap == nullptr || a.out0_f32 || a.act > 1) return EPI_ANY;
+  const int64_t lim = int64_t(1) << 31;
+  if (int64_t(a.zrows) * a.ldz >= lim || int64_t(a.M) * a.ld0 >= lim) return EPI_ANY;
+  if (a.res != nullptr && int64_t(a.M) * a.ldres >= lim) return EPI_ANY;
+  const int v = EPI_Z | (a.bias ? EPI_BIAS : 0) | (a.act == 1 ? EPI_RELU : 0) | (a.res ? EPI_RES : 0);
+  switch (v) {
+    case EPI_Z | EPI_BIAS | EPI_RELU:
+    case EPI_Z | EPI_BIAS | EPI_RES:
+    case EPI_Z | EPI_RELU:
+    case EPI_Z | EPI_RES:
+      return v;
+    default:
+      return EPI_ANY;
+  }
+}
+
+hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
+  GemmArgs a = args;
+  a.epi = epilogue_variant(a);
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (dt == F32) return launch_tiles(gemm_f32_kernel, 64, 64, 256, a, s);
   // All bf16 variants compute every element identically; the choice only

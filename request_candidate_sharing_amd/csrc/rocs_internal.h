@@ -45,6 +45,7 @@ struct GemmArgs {
   int act;
   const void* res;
   int64_t ldres;
+  int epi;  // epilogue variant, set by launch_gemm (callers leave it 0)
 };
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
