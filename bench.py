@@ -73,7 +73,7 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
-ROOFLINE_KERNEL = "gemm_bf16_big_kernel<256, 256, 2, 4, 2>"
+ROOFLINE_KERNEL = "gemm_bf16_mixed_kernel<256, 128>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_glm_mlp.json")
 # sources the candidate GEMM is compiled from (the counters are void once any of them changes)
 GEMM_SRCS = [os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", f)

@@ -466,6 +466,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs
   gemm_tile<BM, BN, WM, WN, NS>(a, (logical / ntn) * BM, (logical % ntn) * BN, smem);
 }
 
+// Two tile heights in one launch: rows [0, M1) in 256-row tiles (whole
+// rounds of one workgroup per CU), then rows [M1, M) in H2-row tiles that
+// fill one more round.  Workgroups are dispatched in order, so the short
+// tiles run last and the final round is not left half empty.
+template <int BN, int H2>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_mixed_kernel(GemmArgs a, int M1) {
+  __shared__ uint4 smem[2 * (256 + BN) * 8];
+  const int ntn = (a.N + BN - 1) / BN;
+  const int n1 = (M1 / 256) * ntn;
+  const int b = blockIdx.x;
+  if (b < n1) {
+    const int logical = xcd_remap(b, n1);
+    gemm_tile<256, BN, 2, 4, 2>(a, (logical / ntn) * 256, (logical % ntn) * BN, smem);
+  } else {
+    const int logical = xcd_remap(b - n1, gridDim.x - n1);
+    gemm_tile<H2, BN, 2, 4, 2>(a, M1 + (logical / ntn) * H2, (logical % ntn) * BN, smem);
+  }
+}
+
 // fp32 path: LDS-tiled SIMT GEMM, 64 x 64 tile, each thread 4 x 4 outputs,
 // K reduced sequentially (one fused multiply-add per k, ascending k).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
@@ -532,23 +551,59 @@ int device_cus() {
   return cus[dev];
 }
 
-// Tile height (256, 192 or 128 rows) for a one-workgroup-per-CU GEMM of M
-// rows and nt column tiles: fewest row-weighted rounds of workgroups, with
-// smaller tiles charged 15% per 64 rows for their extra operand traffic.
-int cand_tile_rows(int M, int nt) {
+// Launch plan for a candidate GEMM (one workgroup per CU, BN = 256): either
+// one tile height for all rows, or 256-row tiles for whole rounds followed
+// by one round of shorter tiles (gemm_bf16_mixed_kernel).  Cost model, in
+// units of a 256-row tile's time, fitted to interleaved timings on the
+// candidate shapes: a tile of h rows costs 0.52 + 0.48 h / 256 (the fixed
+// part is the tile's start, operand traffic and epilogue), and a round of
+// concurrent tiles costs its tile's time.  Measured: N = 1024 (4 column
+// tiles) takes 256-row tiles for 4 rounds and a round of 128-row tiles
+// (116 vs 121 us for 256 rows throughout); N = 512 takes 192-row tiles
+// (109 vs 111 us mixed, 125 us with 256 rows).
+struct CandPlan {
+  int h;             // uniform tile height, or 0 for the mixed plan
+  int M1, h2, grid;  // mixed plan
+};
+
+CandPlan cand_plan(int M, int ntn) {
   const int cus = device_cus();
-  int best = 256;
-  double best_cost = 0.0;
-  for (int bm : {256, 192, 128}) {
-    const long tiles = long((M + bm - 1) / bm) * nt;
-    const long rounds = (tiles + cus - 1) / cus;
-    const double cost = double(rounds) * bm * (1.0 + 0.15 * (256 - bm) / 64.0);
-    if (bm == 256 || cost < best_cost) {
-      best = bm;
+  const auto tile_cost = [](int h) { return 0.52 + 0.48 * h / 256.0; };
+  CandPlan best{256, 0, 0, 0};
+  double best_cost = 1e30;
+  for (int h : {256, 192, 128}) {
+    const long tiles = long((M + h - 1) / h) * ntn;
+    const double cost = double((tiles + cus - 1) / cus) * tile_cost(h);
+    if (cost < best_cost - 1e-9) {
+      best = CandPlan{h, 0, 0, 0};
       best_cost = cost;
     }
   }
+  const int per_round = (cus / ntn) * 256;
+  if (per_round > 0 && M > per_round && M % per_round != 0) {
+    const int M1 = (M / per_round) * per_round, rest = M - M1, slots = cus / ntn;
+    for (int h2 : {64, 128, 192}) {
+      if ((rest + h2 - 1) / h2 > slots) continue;
+      const double cost = double(M1 / per_round) + tile_cost(h2);
+      if (cost < best_cost - 1e-9) {
+        best = CandPlan{0, M1, h2, (M1 / 256) * ntn + ((rest + h2 - 1) / h2) * ntn};
+        best_cost = cost;
+      }
+      break;  // the smallest height that fits one round is the cheapest
+    }
+  }
   return best;
+}
+
+template <int BN>
+hipError_t launch_mixed(const GemmArgs& a, int M1, int h2, int grid, hipStream_t s) {
+  switch (h2) {
+    case 64: hipLaunchKernelGGL((gemm_bf16_mixed_kernel<BN, 64>), dim3(grid), dim3(512), 0, s, a, M1); break;
+    case 128: hipLaunchKernelGGL((gemm_bf16_mixed_kernel<BN, 128>), dim3(grid), dim3(512), 0, s, a, M1); break;
+    case 192: hipLaunchKernelGGL((gemm_bf16_mixed_kernel<BN, 192>), dim3(grid), dim3(512), 0, s, a, M1); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Epilogue variant of a launch: one of the specialised ones when the terms
@@ -580,12 +635,12 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   // candidate shapes (M = 73,704; K, N = 512/1024 both ways, interleaved
   // medians): 256-wide tiles beat 128x128 ones (139 vs 164 us for N =
   // 1024): half the operand traffic from L2 per FLOP.  One workgroup fits
-  // per CU, so the tile height is chosen to fill the last round of
-  // workgroups: for N = 512, 192-row tiles make 768 tiles (3 full rounds on
-  // 256 CUs) instead of 576 (2.25 rounds): 112 vs 134 us.
+  // per CU, so the tile heights are chosen to fill the rounds (cand_plan).
   if (a.M >= 2048) {
     if (a.N > 128) {
-      switch (cand_tile_rows(a.M, (a.N + 255) / 256)) {
+      const CandPlan p = cand_plan(a.M, (a.N + 255) / 256);
+      switch (p.h) {
+        case 0: return launch_mixed<256>(a, p.M1, p.h2, p.grid, s);
         case 192: return launch_tiles(gemm_bf16_big_kernel<192, 256, 2, 4>, 192, 256, 512, a, s);
         case 128: return launch_tiles(gemm_bf16_big_kernel<128, 256, 2, 4>, 128, 256, 512, a, s);
         default: return launch_tiles(gemm_bf16_big_kernel<256, 256, 2, 4>, 256, 256, 512, a, s);

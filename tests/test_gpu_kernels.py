@@ -192,6 +192,45 @@ def test_lcb_candidate_permutation_equivariance(counts, K, N):
     assert torch.equal(y1[pt], y2)
 
 
+@pytest.mark.parametrize("M,K,N", [(19384, 128, 1024),   # 256-row tiles for one round, then 64-row tiles
+                                   (21000, 64, 512),     # one tile height for all rows
+                                   (3000, 520, 264)])
+def test_lcb_candidate_bit_identical_across_launch_plans(M, K, N):
+    # A candidate's output row depends only on its own inputs: the rows of a
+    # large batch (one-workgroup-per-CU tile plans, including the mixed-height
+    # launch) equal, bit for bit, the same rows computed as a small batch
+    # (request-size tiles), at both ends of the batch.
+    from request_candidate_sharing_amd import rocs as Rr
+
+    rng = np.random.default_rng(M + K + N)
+    counts = []
+    while sum(counts) < M:
+        counts.append(int(rng.integers(20, 380)))
+    counts[-1] -= sum(counts) - M
+    bt = S.make_batch(counts)
+    x_c = dev(rand(rng, (M, K), True), torch.bfloat16)
+    w = dev(rand(rng, (N, K), True, K ** -0.5), torch.bfloat16)
+    b = dev(rand(rng, N, True, 0.5), torch.bfloat16)
+    res = dev(rand(rng, (M, N), True), torch.bfloat16)
+    z = torch.randn(len(counts), N, device="cuda")
+    c2r = torch.as_tensor(bt["cand2req"], device="cuda")
+
+    def run(rows, act, use_res):
+        xs, cs = x_c[rows].contiguous(), c2r[rows].contiguous()
+        rs = res[rows].contiguous() if use_res else None
+        y = torch.empty(len(rows), N, dtype=torch.bfloat16, device="cuda")
+        Rr.rocs_lcb_candidate(Rr.batch(len(counts), len(rows), None, cs), Rr.ROCS_BF16, xs, K, K, w, b, N, act, z, N,
+                              rs, N, y, N, Rr.cur_stream())
+        return y
+
+    for act, use_res in ((1, False), (0, True)):
+        full = run(torch.arange(M, device="cuda"), act, use_res)
+        for lo, hi in ((0, 1500), (M - 1500, M)):
+            part = run(torch.arange(lo, hi, device="cuda"), act, use_res)
+            torch.cuda.synchronize()
+            assert torch.equal(full[lo:hi], part), (lo, hi, act, use_res)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", ["layer", "rms"])
 @pytest.mark.parametrize("widths", [(72, 136), (512, 512), (1000, 24), (4096, 40)])
