@@ -88,6 +88,89 @@ __global__ __launch_bounds__(256) void fm_kernel(FmArgs a, int request_mode) {
   }
 }
 
+// Same products with the shape fixed at compile time: NPB x NQB output
+// blocks of 16 x 16, KD k-steps of 32 (D = 32 KD).  Every fragment of the
+// item is requested before the first MFMA, so one memory latency covers the
+// item instead of one per k-step.
+template <int NPB, int NQB, int KD>
+__global__ __launch_bounds__(256) void fm_fast_kernel(FmArgs a, int request_mode) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n_items = request_mode ? a.B_r : a.B_c;
+  if (item >= n_items) return;
+  constexpr int D = 32 * KD;
+  const bf16 *P, *Q1, *Q2;
+  int nP, nQ1, nQ2;
+  bf16* out;
+  int ncols;
+  bool bad = false;
+  if (request_mode) {
+    P = a.x_r + int64_t(item) * a.ldxr;
+    nP = a.n_r;
+    Q1 = P;
+    nQ1 = a.n_r;
+    Q2 = P;
+    nQ2 = 0;
+    out = a.f_r + int64_t(item) * a.ldfr;
+    ncols = a.n_r;
+  } else {
+    int m = a.map ? a.map[item] : item;
+    if ((unsigned)m >= (unsigned)a.map_rows) {
+      bad = true;
+      m = 0;
+    }
+    P = a.x_c + int64_t(item) * a.ldxc;
+    nP = a.n_c;
+    Q1 = a.x_r + int64_t(m) * a.ldxr;
+    nQ1 = a.n_r;
+    Q2 = P;
+    nQ2 = a.n_c;
+    out = a.f_c + int64_t(item) * a.ldfc;
+    ncols = a.n_r + a.n_c;
+  }
+  const int nQ = nQ1 + nQ2;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  bf16x8 pf[NPB][KD], qf[NQB][KD];
+#pragma unroll
+  for (int pb = 0; pb < NPB; ++pb) {
+    const int row = pb * 16 + r16;
+    const bool ok = row < nP;
+    const bf16* rp = P + int64_t(ok ? row : 0) * D + kq;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) pf[pb][kd] = __builtin_bit_cast(bf16x8, frag(rp, ok, kd * 32));
+  }
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = qb * 16 + r16;
+    const bool ok = row < nQ;
+    const bf16* rp = (row < nQ1 ? Q1 + int64_t(row) * D : Q2 + int64_t(ok ? row - nQ1 : 0) * D) + kq;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) qf[qb][kd] = __builtin_bit_cast(bf16x8, frag(rp, ok, kd * 32));
+  }
+  const float nanv = nan_f();
+#pragma unroll
+  for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[qb][kd], pf[pb][kd], acc, 0, 0, 0);
+      const int orow = pb * 16 + r16;
+      const int ocol = qb * 16 + 4 * (lane >> 4);
+      if (orow < nP) {
+        bf16* o = out + int64_t(orow) * ncols + ocol;
+        if (ocol + 4 <= nQ && (ncols & 3) == 0) {
+          bf16x4 pk = {to_bf(bad ? nanv : acc[0]), to_bf(bad ? nanv : acc[1]), to_bf(bad ? nanv : acc[2]),
+                       to_bf(bad ? nanv : acc[3])};
+          *reinterpret_cast<bf16x4*>(o) = pk;
+        } else {
+          for (int j = 0; j < 4; ++j)
+            if (ocol + j < nQ) o[j] = to_bf(bad ? nanv : acc[j]);
+        }
+      }
+    }
+}
+
 // ----------------------------------------------------------------- token-axis LCB
 // Request half: T_R[b] = W_RR X_R[b] (bf16) and Z[b] = W_CR X_R[b] (fp32), once
 // per request.  One workgroup per request; thread item = (output token t, 8
@@ -196,11 +279,134 @@ __global__ __launch_bounds__(256) void tok_candidate_kernel(TokLcbArgs a, int cp
   }
 }
 
+// Candidate half on the matrix cores: per candidate, T_C = W_CC X_C[i] is a
+// [t_c x n_c] x [n_c x D] product, i.e. TB x (D / 32) blocks of
+// v_mfma_f32_32x32x16_bf16 with KS k-steps of 16 input tokens (zero-padded).
+// Wave w owns the 32 dims d = 32w..32w+31: its A operand is X_C[i]^T (row d,
+// 8 consecutive input tokens per lane half, gathered straight from memory),
+// its B operand W_CC (row t), so a lane ends with 4 consecutive d of one t.
+// The fp32 request contribution Z[m] for those positions stays in registers
+// while consecutive candidates share m.  The rounded block goes through an
+// LDS stage and leaves as contiguous 16-byte chunks of the candidate's
+// [t_c x D] output.
+template <int TB, int KS>
+__global__ __launch_bounds__(256) void tok_candidate_mfma_kernel(TokLcbArgs a, int cpw) {
+  extern __shared__ uint4 smem_raw[];
+  bf16* stage = reinterpret_cast<bf16*>(smem_raw);  // [t_c][D + 8]
+  const int D = a.dim, nc = a.n_c, tc = a.t_c;
+  const int SP = D + 8;
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int db = threadIdx.x >> 6;
+  const int d = db * 32 + l32;  // this lane's A-operand row
+  bf16x8 wf[TB][KS];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = tb * 32 + l32, k = ks * 16 + 8 * h + e;
+        wf[tb][ks][e] = (t < tc && k < nc) ? a.w_cc[t * nc + k] : bf16(0.f);
+      }
+  float zc[TB][4][4];
+  int zm = -2;
+  const int i0 = blockIdx.x * cpw;
+  const int i1 = min(i0 + cpw, a.B_c);
+  const int nch = tc * (D / 8);
+  for (int i = i0; i < i1; ++i) {
+    const bf16* x = a.x_c + int64_t(i) * a.ldxc;
+    bf16x8 xf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = ks * 16 + 8 * h + e;
+        xf[ks][e] = k < nc ? x[k * D + d] : bf16(0.f);
+      }
+    int m = a.map ? a.map[i] : i;
+    if ((unsigned)m >= (unsigned)a.map_rows) m = -1;
+    if (m != zm) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int t = tb * 32 + l32;
+          float4 v = make_float4(nan_f(), nan_f(), nan_f(), nan_f());
+          if (m >= 0 && t < tc)
+            v = *reinterpret_cast<const float4*>(a.z + int64_t(m) * (int64_t(tc) * D) + int64_t(t) * D + db * 32 +
+                                                 8 * g + 4 * h);
+          zc[tb][g][0] = v.x; zc[tb][g][1] = v.y; zc[tb][g][2] = v.z; zc[tb][g][3] = v.w;
+        }
+      zm = m;
+    }
+    f32x16 acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[ks], wf[tb][ks], acc[tb], 0, 0, 0);
+    }
+    __syncthreads();  // the previous candidate's stage has been read
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int t = tb * 32 + l32;
+      if (t < tc)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 pk = {to_bf(acc[tb][4 * g] + zc[tb][g][0]), to_bf(acc[tb][4 * g + 1] + zc[tb][g][1]),
+                       to_bf(acc[tb][4 * g + 2] + zc[tb][g][2]), to_bf(acc[tb][4 * g + 3] + zc[tb][g][3])};
+          *reinterpret_cast<bf16x4*>(stage + t * SP + db * 32 + 8 * g + 4 * h) = pk;
+        }
+    }
+    __syncthreads();
+    bf16* y = a.y_c + int64_t(i) * a.ldyc;
+    for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+      const int t = c / (D / 8), d8 = c - t * (D / 8);
+      *reinterpret_cast<uint4*>(y + t * D + d8 * 8) = *reinterpret_cast<const uint4*>(stage + t * SP + d8 * 8);
+    }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+using FmKernel = void (*)(FmArgs, int);
+
+// fm_fast_kernel for NPB x NQB blocks and D = 32 KD, when instantiated.
+template <int NPB>
+FmKernel fm_fast_for(int nqb, int kd) {
+  const int key = nqb * 16 + kd;
+  switch (key) {
+    case 1 * 16 + 2: return fm_fast_kernel<NPB, 1, 2>;
+    case 2 * 16 + 2: return fm_fast_kernel<NPB, 2, 2>;
+    case 3 * 16 + 2: return fm_fast_kernel<NPB, 3, 2>;
+    case 4 * 16 + 2: return fm_fast_kernel<NPB, 4, 2>;
+    case 1 * 16 + 4: return fm_fast_kernel<NPB, 1, 4>;
+    case 2 * 16 + 4: return fm_fast_kernel<NPB, 2, 4>;
+    case 3 * 16 + 4: return fm_fast_kernel<NPB, 3, 4>;
+    case 4 * 16 + 4: return fm_fast_kernel<NPB, 4, 4>;
+    default: return nullptr;
+  }
+}
+
+FmKernel fm_kernel_for(int np, int nq, int dim) {
+  if (dim % 32 != 0) return fm_kernel;
+  const int npb = (np + 15) / 16, nqb = (nq + 15) / 16, kd = dim / 32;
+  FmKernel k = nullptr;
+  if (npb == 1) k = fm_fast_for<1>(nqb, kd);
+  if (npb == 2) k = fm_fast_for<2>(nqb, kd);
+  return k ? k : fm_kernel;
+}
+
 }  // namespace
 
 hipError_t launch_fm(const FmArgs& a, hipStream_t s) {
-  if (a.B_r > 0) hipLaunchKernelGGL(fm_kernel, dim3((a.B_r + 3) / 4), dim3(256), 0, s, a, 1);
-  if (a.B_c > 0) hipLaunchKernelGGL(fm_kernel, dim3((a.B_c + 3) / 4), dim3(256), 0, s, a, 0);
+  if (a.B_r > 0)
+    hipLaunchKernelGGL(fm_kernel_for(a.n_r, a.n_r, a.dim), dim3((a.B_r + 3) / 4), dim3(256), 0, s, a, 1);
+  if (a.B_c > 0)
+    hipLaunchKernelGGL(fm_kernel_for(a.n_c, a.n_r + a.n_c, a.dim), dim3((a.B_c + 3) / 4), dim3(256), 0, s, a, 0);
   return hipGetLastError();
 }
 
@@ -211,8 +417,39 @@ hipError_t launch_token_lcb_request(const TokLcbArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+
+template <int TB>
+hipError_t launch_tok_mfma(const TokLcbArgs& a, int ks, hipStream_t s) {
+  const int cpw = 16;
+  const size_t lds = size_t(TB * 32) * (a.dim + 8) * 2;
+  const dim3 grid((a.B_c + cpw - 1) / cpw), block(64 * (a.dim / 32));
+  switch (ks) {
+    case 1: hipLaunchKernelGGL((tok_candidate_mfma_kernel<TB, 1>), grid, block, lds, s, a, cpw); break;
+    case 2: hipLaunchKernelGGL((tok_candidate_mfma_kernel<TB, 2>), grid, block, lds, s, a, cpw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_token_lcb_candidate(const TokLcbArgs& a, hipStream_t s) {
   if (a.B_c <= 0) return hipSuccess;
+  // Matrix-core path: D a multiple of 32 up to 128 (one wave per 32 dims),
+  // up to 128 output and 32 input tokens, 16-byte aligned output rows.
+  const bool mfma_ok = a.dim % 32 == 0 && a.dim <= 128 && a.t_c <= 128 && a.n_c <= 32 &&
+                       (reinterpret_cast<uintptr_t>(a.y_c) & 15) == 0 && a.ldyc % 8 == 0;
+  if (mfma_ok) {
+    const int tb = (a.t_c + 31) / 32, ks = (a.n_c + 15) / 16;
+    switch (tb) {
+      case 1: return launch_tok_mfma<1>(a, ks, s);
+      case 2: return launch_tok_mfma<2>(a, ks, s);
+      case 3: return launch_tok_mfma<3>(a, ks, s);
+      case 4: return launch_tok_mfma<4>(a, ks, s);
+      default: break;
+    }
+  }
   const int items = a.t_c * (a.dim / 8);
   const int it = (items + 255) / 256;
   const int cpw = 8;

@@ -393,12 +393,16 @@ def test_encode_kv_parity():
 # ---------------------------------------------------------------- FM / token LCB
 
 
-def test_fm_masked_parity():
+@pytest.mark.parametrize("nr,nc,D", [(32, 16, 128),   # fixed-shape kernel, 1 x 3 blocks, 4 k-steps
+                                     (8, 4, 64),      # fixed-shape kernel, padded rows and columns
+                                     (20, 12, 96),    # generic kernel (D not 32 * {2, 4})
+                                     (40, 24, 64)])   # two row blocks for the request items
+def test_fm_masked_parity(nr, nc, D):
     R = _R()
-    rng = np.random.default_rng(21)
+    rng = np.random.default_rng(21 + nr + nc + D)
     counts = [3, 0, 70, 140, 1]
     bt = S.make_batch(counts)
-    B, Bc, nr, nc, D = len(counts), sum(counts), 32, 16, 128
+    B, Bc = len(counts), sum(counts)
     xr, xc = rand(rng, (B, nr, D), True, 0.3), rand(rng, (Bc, nc, D), True, 0.3)
     fr = torch.empty(B, nr * nr, dtype=torch.bfloat16, device="cuda")
     fc = torch.empty(Bc, nc * (nr + nc), dtype=torch.bfloat16, device="cuda")
@@ -413,14 +417,18 @@ def test_fm_masked_parity():
     assert rel_err(to_np(fr), ref_r_req) <= TOL_BF16
 
 
-def test_token_lcb_parity():
+@pytest.mark.parametrize("nr,nc,D,tr,tc", [(32, 16, 128, 64, 64),  # matrix-core path, 2 t-blocks, 1 k-step
+                                            (8, 4, 64, 16, 16),      # padded tokens
+                                            (16, 24, 96, 8, 80),     # 3 t-blocks, 2 k-steps
+                                            (12, 8, 40, 8, 24)])     # D not a multiple of 32: FMA path
+def test_token_lcb_parity(nr, nc, D, tr, tc):
     R = _R()
-    rng = np.random.default_rng(22)
+    rng = np.random.default_rng(22 + nr + nc + D + tc)
     counts = [3, 0, 70, 17, 1, 9, 40]
     bt = S.make_batch(counts)
-    B, Bc, nr, nc, D, tr, tc = len(counts), sum(counts), 32, 16, 128, 64, 64
+    B, Bc = len(counts), sum(counts)
     xr, xc = rand(rng, (B, nr, D), True, 0.3), rand(rng, (Bc, nc, D), True, 0.3)
-    W = rand(rng, (tr + tc, nr + nc), True, 48 ** -0.5)
+    W = rand(rng, (tr + tc, nr + nc), True, (nr + nc) ** -0.5)
     yr = torch.empty(B, tr * D, dtype=torch.bfloat16, device="cuda")
     yc = torch.empty(Bc, tc * D, dtype=torch.bfloat16, device="cuda")
     z = torch.empty(B, tc * D, dtype=torch.float32, device="cuda")
