@@ -30,7 +30,7 @@ __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chu
 __device__ __forceinline__ int vt_off(int dh, int unit) { return dh * 16 + (unit ^ (dh & 15)); }
 
 template <bool VT>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
   __shared__ uint4 sK[2][KC * 8];
   __shared__ uint2 sV[2][DH * 16];
 
