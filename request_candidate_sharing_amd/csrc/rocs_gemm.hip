@@ -156,12 +156,14 @@ __device__ __forceinline__ void epilogue1(const GemmArgs& a, int m, int c, float
 // Per-wave LDS stage of the transposing epilogue: 32 rows of up to 64 fp32
 // accumulators (two 32x32 blocks), rows padded by 16 bytes (conflict-free
 // both ways).  Wider wave tiles go through it two blocks at a time.
-template <int FN>
-constexpr int stage_blocks() { return FN > 2 ? 2 : FN; }
-template <int FN>
-constexpr int stage_pitch() { return stage_blocks<FN>() * 32 + 4; }
-template <int FN>
-constexpr int stage_floats() { return 32 * stage_pitch<FN>(); }
+template <int FN, int JWM = 2>
+constexpr int stage_blocks() { return FN > JWM ? JWM : FN; }
+template <int FN, int JWM = 2>
+constexpr int stage_pitch() { return stage_blocks<FN, JWM>() * 32 + 4; }
+template <int FN, int JWM = 2>
+constexpr int stage_floats() { return 32 * stage_pitch<FN, JWM>(); }
+template <int FN, int JWM = 2>
+__device__ __forceinline__ int stage_at(int r, int c) { return r * stage_pitch<FN, JWM>() + c; }
 
 // Epilogue variants.  EPI_ANY tests every optional term at run time; the
 // others are fixed at compile time for the candidate GEMMs of the layer
@@ -184,13 +186,12 @@ enum : int {
 // time.  All loads of a pass (map entries, Z rows, residual) are issued
 // before its arithmetic and stores.  The arithmetic is the edge path's:
 // acc + Z + bias, act, + residual, one rounding.
-template <int FN, int EPI = EPI_ANY>
+template <int FN, int EPI = EPI_ANY, int JWM = 2>
 __device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, int nb, int lane,
                                                  const f32x16 (&row)[FN], float* stage) {
   constexpr bool ANY = EPI == EPI_ANY;
-  constexpr int JW = stage_blocks<FN>();
+  constexpr int JW = stage_blocks<FN, JWM>();
   static_assert(FN % JW == 0, "column blocks must pair up");
-  constexpr int P = stage_pitch<FN>();
   constexpr int LPR = JW * 8;     // lanes per row
   constexpr int RPI = 64 / LPR;   // rows per pass
   constexpr int NP = 32 / RPI;    // passes per block-row
@@ -231,7 +232,7 @@ __device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, i
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& c = row[jg * JW + jj];
-        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
+        *reinterpret_cast<f32x4*>(stage + stage_at<FN, JWM>(lane & 31, jj * 32 + 8 * g + 4 * hk)) =
             f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
       }
     __builtin_amdgcn_wave_barrier();
@@ -249,7 +250,7 @@ __device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, i
     f32x4 sv[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      sv[p] = *reinterpret_cast<const f32x4*>(stage + (p * RPI + rl) * P + (lane % LPR) * 4);
+      sv[p] = *reinterpret_cast<const f32x4*>(stage + stage_at<FN, JWM>(p * RPI + rl, (lane % LPR) * 4));
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -282,11 +283,10 @@ __device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, i
 // Edge block-rows (N tail, the split between the two outputs, fp32 output):
 // the block-row goes through the LDS stage too, then one element per lane
 // at a time through epilogue1 (no register array is indexed at run time).
-template <int FN>
+template <int FN, int JWM = 2>
 __device__ __forceinline__ void store_row_edge(const GemmArgs& a, int mrow0, int nb, int lane,
                                                const f32x16 (&row)[FN], float* stage) {
-  constexpr int JW = stage_blocks<FN>();
-  constexpr int P = stage_pitch<FN>();
+  constexpr int JW = stage_blocks<FN, JWM>();
   constexpr int W = JW * 32;
   const int hk = lane >> 5;
 #pragma unroll
@@ -296,46 +296,46 @@ __device__ __forceinline__ void store_row_edge(const GemmArgs& a, int mrow0, int
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& c = row[jg * JW + jj];
-        *reinterpret_cast<f32x4*>(stage + (lane & 31) * P + jj * 32 + 8 * g + 4 * hk) =
+        *reinterpret_cast<f32x4*>(stage + stage_at<FN, JWM>(lane & 31, jj * 32 + 8 * g + 4 * hk)) =
             f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
       }
     __builtin_amdgcn_wave_barrier();
     for (int e = lane; e < 32 * W; e += 64) {
       const int r = e / W, c = e % W;
-      epilogue1<bf16>(a, mrow0 + r, nb + jg * W + c, stage[r * P + c]);
+      epilogue1<bf16>(a, mrow0 + r, nb + jg * W + c, stage[stage_at<FN, JWM>(r, c)]);
     }
     __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int FN, int EPI>
+template <int FN, int EPI, int JWM>
 __device__ __forceinline__ void store_row(const GemmArgs& a, int mrow0, int nb, int lane, const f32x16 (&row)[FN],
                                           float* stage) {
   const bool interior = (nb + FN * 32 <= a.N) && (nb + FN * 32 <= a.n_split) && !a.out0_f32;
   if (interior)
-    store_row_staged<FN, EPI>(a, mrow0, nb, lane, row, stage);
+    store_row_staged<FN, EPI, JWM>(a, mrow0, nb, lane, row, stage);
   else
-    store_row_edge(a, mrow0, nb, lane, row, stage);
+    store_row_edge<FN, JWM>(a, mrow0, nb, lane, row, stage);
 }
 
-template <int EPI, int FM, int FN>
+template <int EPI, int JWM, int FM, int FN>
 __device__ __forceinline__ void store_blocks_as(const GemmArgs& a, int mb, int nb, int lane,
                                                 const f32x16 (&acc)[FM][FN], float* stage) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) store_row<FN, EPI>(a, mb + i * 32, nb, lane, acc[i], stage);
+  for (int i = 0; i < FM; ++i) store_row<FN, EPI, JWM>(a, mb + i * 32, nb, lane, acc[i], stage);
 }
 
 // The epilogue variant is uniform per launch: one switch, then straight-line
 // code without per-element feature tests.
-template <int FM, int FN>
+template <int JWM = 2, int FM, int FN>
 __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, const f32x16 (&acc)[FM][FN],
                                              float* stage) {
   switch (a.epi) {
-    case EPI_Z | EPI_BIAS | EPI_RELU: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RELU>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_BIAS | EPI_RES: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RES>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_RELU: store_blocks_as<EPI_Z | EPI_RELU>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_RES: store_blocks_as<EPI_Z | EPI_RES>(a, mb, nb, lane, acc, stage); break;
-    default: store_blocks_as<EPI_ANY>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_BIAS | EPI_RELU: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_BIAS | EPI_RES: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_RELU: store_blocks_as<EPI_Z | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
+    case EPI_Z | EPI_RES: store_blocks_as<EPI_Z | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
+    default: store_blocks_as<EPI_ANY, JWM>(a, mb, nb, lane, acc, stage); break;
   }
 }
 
@@ -378,82 +378,104 @@ __device__ __forceinline__ void wait_slabs(int newer) {
   }
 }
 
+// This wave's share of the slab DMA for one BM x BN tile: PER
+// wave-instructions per 64-wide slab, each filling 1 KB of the ring (8 rows
+// of 128 B); lane i fetches the global chunk that the row swizzle places at
+// its LDS slot.  Chunks past K come from the zero page.
+template <int BM, int BN, int NW>
+struct SlabFeed {
+  static constexpr int CPR = 8, RPI = 8;
+  static constexpr int RB = (BM + BN) / RPI;
+  static_assert(RB % NW == 0, "row blocks must divide among waves");
+  static constexpr int PER = RB / NW;
+  const bf16* src[PER];
+  int kofs[PER];
+  __device__ __forceinline__ void init(const GemmArgs& a, const WeightSegs& ws, int m0, int n0, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int r = (wave * PER + j) * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ swz<CPR>(r);
+      kofs[j] = chunk * 8;
+      if (r < BM)
+        src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
+      else
+        src[j] = weight_row(ws.w0, ws.w1, ws.w2, ws.w3, ws.e0, ws.e1, ws.e2, a.ldw, min(n0 + r - BM, a.N - 1)) +
+                 chunk * 8;
+    }
+  }
+  __device__ __forceinline__ void issue(int K, const void* zero, int k0, uint4* slot, int wave) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const void* p = (k0 + kofs[j] < K) ? static_cast<const void*>(src[j] + k0) : zero;
+      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(slot + (wave * PER + j) * 64), 16, 0, 0);
+    }
+  }
+};
+
+// The zero page's address comes from the GOT.  Loaded inside a loop, that
+// scalar load (out of order with LDS reads on the same counter) would turn
+// every fragment wait into a full lgkmcnt(0); pinned in SGPRs by the caller,
+// it is loaded once.
+__device__ __forceinline__ const void* pinned_zero_page() {
+  const void* zero = g_zero_page;
+  asm volatile("" : "+s"(zero));
+  return zero;
+}
+
 // One BM x BN output tile at (m0, n0) on a workgroup of WM x WN waves, with
-// the ring (NS slots of BM + BN rows of one 64-wide slab) at smem.
+// the ring (NS slots of BM + BN rows of one 64-wide slab) at smem; slab kb
+// lives in slot kb % NS.
 template <int BM, int BN, int WM, int WN, int NS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uint4* smem) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
-  constexpr int RPI = 64 / CPR;             // rows per wave-instruction
-  constexpr int RB = (BM + BN) / RPI;       // wave-instructions per slab
-  static_assert(RB % NW == 0, "row blocks must divide among waves");
-  constexpr int PER = RB / NW;
-  static_assert(NS >= 2 && PER * (NS - 2) < 64, "ring depth");
-  constexpr int SLAB = (BM + BN) * CPR;     // uint4 per ring slot
-  static_assert(NW * stage_floats<FN>() * 4 <= NS * SLAB * 16, "epilogue stage exceeds the ring");
+  constexpr int CPR = BK / 8;
+  constexpr int SLOT = (BM + BN) * CPR;
+  static_assert(NW * stage_floats<FN>() * 4 <= NS * SLOT * 16, "epilogue stage exceeds the ring");
+  using Feed = SlabFeed<BM, BN, NW>;
+  static_assert(NS >= 2 && Feed::PER * (NS - 2) < 64, "ring depth");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-
-  // The zero page's address comes from the GOT.  Loaded inside the loop, that
-  // scalar load (out of order with LDS reads on the same counter) would turn
-  // every fragment wait into a full lgkmcnt(0); pinned in SGPRs here, it is
-  // loaded once.  The weight segment table is pinned the same way, outside
-  // the lane-dependent row selection below.
-  const void* zero = g_zero_page;
-  asm volatile("" : "+s"(zero));
+  const void* zero = pinned_zero_page();
   const WeightSegs ws = weight_segs(a);
-  const bf16* src[PER];
-  int kofs[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int r = (wave * PER + j) * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz<CPR>(r);
-    kofs[j] = chunk * 8;
-    if (r < BM)
-      src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
-    else
-      src[j] = weight_row(ws.w0, ws.w1, ws.w2, ws.w3, ws.e0, ws.e1, ws.e2, a.ldw, min(n0 + r - BM, a.N - 1)) +
-               chunk * 8;
-  }
-  auto issue = [&](int k0, int st) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const void* p = (k0 + kofs[j] < a.K) ? static_cast<const void*>(src[j] + k0) : zero;
-      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(smem + st * SLAB + (wave * PER + j) * 64), 16, 0, 0);
-    }
-  };
+  auto slot = [&](int kb) { return smem + (kb % NS) * SLOT; };
 
+  Feed feed;
+  feed.init(a, ws, m0, n0, wave, lane);
   f32x16 acc[FM][FN];
   zero_acc(acc);
 
   const int nk = (a.K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s * BK, s);
+    if (s < nk) feed.issue(a.K, zero, s * BK, slot(s), wave);
 
   const int xr0 = wm * WTM + (lane & 31);
   const int wr0 = BM + wn * WTN + (lane & 31);
   Frags<FM, FN> fr;
-  for (int kb = 0; kb < nk; ++kb) {
+  for (int kb = 0; kb < nk - 1; ++kb) {
     // Slab kb has landed once at most min(NS-2, nk-1-kb) newer slabs (PER
     // instructions each, returned in order) are still outstanding.
-    wait_slabs<PER, NS - 2>(min(NS - 2, nk - 1 - kb));
+    wait_slabs<Feed::PER, NS - 2>(min(NS - 2, nk - 1 - kb));
     // every wave's part of slab kb is in LDS, and every wave is done with
-    // slab kb-1 (its last step's fragments are in registers), whose buffer
+    // slab kb-1 (its last step's fragments are in registers), whose slot
     // the next issue refills
     __syncthreads();
-    if (kb + NS - 1 < nk) issue((kb + NS - 1) * BK, (kb + NS - 1) % NS);
-    const uint4* sl = smem + (kb % NS) * SLAB;
+    if (kb + NS - 1 < nk) feed.issue(a.K, zero, (kb + NS - 1) * BK, slot(kb + NS - 1), wave);
+    const uint4* sl = slot(kb);
     mfma_slab_carry<FM, FN, CPR, CPR>(fr, kb > 0, sl, wr0, sl, xr0, lane >> 5, acc);
   }
-  if (nk > 0) mfma_frags(fr, 1, acc);
-  wait_vmcnt<0>();
-  __syncthreads();  // the epilogue reuses the ring as its staging buffer
-  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc,
-               reinterpret_cast<float*>(smem) + wave * stage_floats<FN>());
+  if (nk > 0) {  // the last slab, then the carried step
+    wait_vmcnt<0>();
+    __syncthreads();
+    const uint4* sl = slot(nk - 1);
+    mfma_slab_carry<FM, FN, CPR, CPR>(fr, nk > 1, sl, wr0, sl, xr0, lane >> 5, acc);
+    mfma_frags(fr, 1, acc);
+  }
+  __syncthreads();  // every wave is done reading the ring: the epilogue stages in it
+  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc, reinterpret_cast<float*>(smem) + wave * stage_floats<FN>());
 }
 
 // One tile per workgroup, tiles in XCD-aware order.
