@@ -507,6 +507,65 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_mixed_kernel(GemmArgs a, int
   }
 }
 
+// Request-side GEMMs with a long K (K >= 1024; few output tiles, each a long
+// chain of slabs): 32 x 32 output tiles, four waves per tile, wave w reducing the
+// contiguous K quarter [w nk / 4, (w + 1) nk / 4) through a ring of its own
+// (no workgroup barrier in the loop).  The four fp32 partial tiles are then
+// added in a fixed order, ((p0 + p1) + p2) + p3, and wave 0 runs the
+// epilogue.  The result is deterministic; it is summed in a different order
+// than the single-chain kernels, which these request batches never use.
+template <int NS>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a) {
+  constexpr int BM = 32, BN = 32, BK = 64, CPR = 8, SLOT = (BM + BN) * CPR, SPLIT = 4;
+  __shared__ uint4 smem[SPLIT * NS * SLOT];
+  using Feed = SlabFeed<BM, BN, 1>;
+  static_assert(Feed::PER * (NS - 2) < 64, "ring depth");
+  const int ntn = (a.N + BN - 1) / BN;
+  const int ntm = (a.M + BM - 1) / BM;
+  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
+  const int m0 = (logical / ntn) * BM, n0 = (logical % ntn) * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const void* zero = pinned_zero_page();
+  const WeightSegs ws = weight_segs(a);
+  uint4* ring = smem + wave * NS * SLOT;
+  auto slot = [&](int i) { return ring + (i % NS) * SLOT; };
+
+  const int nk = (a.K + BK - 1) / BK;
+  const int k_lo = (wave * nk) / SPLIT, k_hi = ((wave + 1) * nk) / SPLIT;
+  const int n = k_hi - k_lo;  // slabs of this wave
+  Feed feed;
+  feed.init(a, ws, m0, n0, 0, lane);
+  f32x16 acc[1][1];
+  zero_acc(acc);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < n) feed.issue(a.K, zero, (k_lo + i) * BK, slot(i), 0);
+  Frags<1, 1> fr;
+  for (int i = 0; i < n; ++i) {
+    wait_slabs<Feed::PER, NS - 2>(min(NS - 2, n - 1 - i));
+    __builtin_amdgcn_wave_barrier();
+    if (i + NS - 1 < n) feed.issue(a.K, zero, (k_lo + i + NS - 1) * BK, slot(i + NS - 1), 0);
+    const uint4* sl = slot(i);
+    mfma_slab_carry<1, 1, CPR, CPR>(fr, i > 0, sl, BM + (lane & 31), sl, lane & 31, lane >> 5, acc);
+  }
+  if (n > 0) mfma_frags(fr, 1, acc);
+  __syncthreads();  // every wave is done with its ring: the partials go there
+  float* part = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = part[r * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < SPLIT; ++w) v += part[(w * 16 + r) * 64 + lane];
+    acc[0][0][r] = v;
+  }
+  store_blocks(a, m0, n0, lane, acc, part + SPLIT * 16 * 64);
+}
+
 // fp32 path: LDS-tiled SIMT GEMM, 64 x 64 tile, each thread 4 x 4 outputs,
 // K reduced sequentially (one fused multiply-add per k, ascending k).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
@@ -673,7 +732,11 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   // Request batches (M <= a few hundred): the weights stream from HBM once
   // and K/64 slabs run in sequence, so the time is slab latency.  One-wave
   // 32x32 tiles put enough workgroups on the chip (B_r = 256, N = 1024:
-  // 256 of them), each with seven slabs (56 KB) in flight.
+  // 256 of them), each with seven slabs (56 KB) in flight.  Longer chains
+  // split K over four waves per tile (measured, M = 128, N = 2048, K = 8960:
+  // 62 -> 25 us; M = 256, N = 1024, K = 1024: 8.3 -> 5.2 us; at K = 512 the
+  // single chain is faster, 6.1 vs 7.5 us).
+  if (a.K >= 1024) return launch_tiles(gemm_bf16_splitk_kernel<4>, 32, 32, 256, a, s);
   return launch_tiles(gemm_bf16_big_kernel<32, 32, 1, 1, 8>, 32, 32, 64, a, s);
 }
 

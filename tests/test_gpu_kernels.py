@@ -117,6 +117,9 @@ def lcb_case(counts, d_in_r, d_in_c, d_out_r, d_out_c, dt, act, seed, bias=True,
         ([3000], (512, 1024, 64, 512)),
         # many tiny requests: a 256-row tile spans more request rows than it stages in LDS
         ([3] * 700 + [0, 1] * 40, (64, 128, 32, 384)),
+        # long request K: four waves per request tile split K (uneven quarters, K tail)
+        ([5, 0, 40, 7], (2120, 64, 40, 72)),
+        ([60, 3], (1032, 96, 64, 200)),
     ],
 )
 def test_lcb_forward_parity(dt, counts, dims):
