@@ -171,6 +171,75 @@ __global__ __launch_bounds__(256) void fm_fast_kernel(FmArgs a, int request_mode
     }
 }
 
+// Candidate items with n_C <= 16 and n_R a multiple of 16 (NQR blocks of
+// request rows), D = 32 KD.  A wave walks IPW consecutive candidates and
+// keeps the fragments of its request's tokens X_R[m] in registers while m
+// is unchanged; the candidate's own fragments serve both as the row
+// operand and as the last column block (the candidate x candidate part),
+// and the next candidate's are requested before the current one's MFMAs.
+// The MFMA sequence of every output block is fm_fast_kernel's, so the
+// results are bit-identical to it.
+template <int NQR, int KD>
+__global__ __launch_bounds__(256) void fm_cand_kernel(FmArgs a, int ipw) {
+  constexpr int D = 32 * KD;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int i0 = (blockIdx.x * 4 + wave) * ipw;
+  const int i1 = min(i0 + ipw, a.B_c);
+  if (i0 >= i1) return;
+  const int nc = a.n_c, nr = a.n_r, ncols = nr + nc;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const bool prow = r16 < nc;
+  auto load_p = [&](int i, bf16x8 (&pf)[KD]) {
+    const bf16* rp = a.x_c + int64_t(i) * a.ldxc + int64_t(prow ? r16 : 0) * D + kq;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) pf[kd] = __builtin_bit_cast(bf16x8, frag(rp, prow, kd * 32));
+  };
+  bf16x8 rq[NQR][KD];
+  bf16x8 pf[KD], pn[KD];
+  int mc = -1;
+  load_p(i0, pf);
+  const float nanv = nan_f();
+  for (int i = i0; i < i1; ++i) {
+    if (i + 1 < i1) load_p(i + 1, pn);
+    int m = a.map ? a.map[i] : i;
+    const bool bad = (unsigned)m >= (unsigned)a.map_rows;
+    if (bad) m = 0;
+    if (m != mc) {
+#pragma unroll
+      for (int qb = 0; qb < NQR; ++qb) {
+        const bf16* rp = a.x_r + int64_t(m) * a.ldxr + int64_t(qb * 16 + r16) * D + kq;
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) rq[qb][kd] = __builtin_bit_cast(bf16x8, frag(rp, true, kd * 32));
+      }
+      mc = m;
+    }
+    bf16* out = a.f_c + int64_t(i) * a.ldfc;
+    const int orow = r16;
+#pragma unroll
+    for (int qb = 0; qb <= NQR; ++qb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb < NQR ? rq[qb][kd] : pf[kd], pf[kd], acc, 0, 0, 0);
+      const int ocol = qb * 16 + 4 * (lane >> 4);
+      if (orow < nc) {
+        bf16* o = out + int64_t(orow) * ncols + ocol;
+        if (ocol + 4 <= ncols && (ncols & 3) == 0) {
+          bf16x4 pk = {to_bf(bad ? nanv : acc[0]), to_bf(bad ? nanv : acc[1]), to_bf(bad ? nanv : acc[2]),
+                       to_bf(bad ? nanv : acc[3])};
+          *reinterpret_cast<bf16x4*>(o) = pk;
+        } else {
+          for (int j = 0; j < 4; ++j)
+            if (ocol + j < ncols) o[j] = to_bf(bad ? nanv : acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) pf[kd] = pn[kd];
+  }
+}
+
 // ----------------------------------------------------------------- token-axis LCB
 // Request half: T_R[b] = W_RR X_R[b] (bf16) and Z[b] = W_CR X_R[b] (fp32), once
 // per request.  One workgroup per request; thread item = (output token t, 8
@@ -275,6 +344,61 @@ __global__ __launch_bounds__(256) void tok_candidate_kernel(TokLcbArgs a, int cp
 #pragma unroll
       for (int j = 0; j < 8; ++j) pk[j] = to_bf(acc[j] + zc[q][j]);
       *reinterpret_cast<bf16x8*>(a.y_c + int64_t(i) * a.ldyc + int64_t(t) * D + d0) = pk;
+    }
+  }
+}
+
+// Request half on the matrix cores: per request, [T_R; Z] = [W_RR; W_CR]
+// X_R[b], a [(t_r + t_c) x n_r] x [n_r x D] product (TB blocks of 32 output
+// tokens, KS k-steps of 16 input tokens, zero-padded).  Wave w owns the 32
+// dims d = 32w..32w+31 (A operand X_R[b]^T, gathered from memory; B operand
+// the stacked weights).  Rows below t_r are T_R (bf16), the rest Z (fp32),
+// stored straight from the MFMA layout: one workgroup per request, few of
+// them, so the stores' row pattern does not matter.
+template <int TB, int KS>
+__global__ __launch_bounds__(256) void tok_request_mfma_kernel(TokLcbArgs a) {
+  const int D = a.dim, nr = a.n_r, tr = a.t_r, tc = a.t_c, T = tr + tc;
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int db = threadIdx.x >> 6;
+  const int d = db * 32 + l32;
+  const int b = blockIdx.x;
+  const bf16* x = a.x_r + int64_t(b) * a.ldxr;
+  bf16x8 xf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = ks * 16 + 8 * h + e;
+      xf[ks][e] = k < nr ? x[k * D + d] : bf16(0.f);
+    }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t = tb * 32 + l32;
+    const bf16* w = t < tr ? a.w_rr + int64_t(t) * nr : a.w_cr + int64_t(t - tr) * nr;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 wf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = ks * 16 + 8 * h + e;
+        wf[e] = (t < T && k < nr) ? w[k] : bf16(0.f);
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[ks], wf, acc, 0, 0, 0);
+    }
+    if (t >= T) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * h;
+      if (t < tr) {
+        bf16x4 pk = {to_bf(acc[4 * g]), to_bf(acc[4 * g + 1]), to_bf(acc[4 * g + 2]), to_bf(acc[4 * g + 3])};
+        *reinterpret_cast<bf16x4*>(a.y_r + int64_t(b) * a.ldyr + int64_t(t) * D + d0) = pk;
+      } else {
+        *reinterpret_cast<float4*>(a.z + int64_t(b) * (int64_t(tc) * D) + int64_t(t - tr) * D + d0) =
+            make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+      }
     }
   }
 }
@@ -405,13 +529,51 @@ FmKernel fm_kernel_for(int np, int nq, int dim) {
 hipError_t launch_fm(const FmArgs& a, hipStream_t s) {
   if (a.B_r > 0)
     hipLaunchKernelGGL(fm_kernel_for(a.n_r, a.n_r, a.dim), dim3((a.B_r + 3) / 4), dim3(256), 0, s, a, 1);
-  if (a.B_c > 0)
-    hipLaunchKernelGGL(fm_kernel_for(a.n_c, a.n_r + a.n_c, a.dim), dim3((a.B_c + 3) / 4), dim3(256), 0, s, a, 0);
+  if (a.B_c <= 0) return hipGetLastError();
+  // candidates: the request-caching kernel for n_C <= 16, n_R in {16, 32, 48}
+  // and D in {64, 128}; otherwise one item per wave
+  const int nqr = a.n_r / 16;
+  if (a.n_c <= 16 && a.n_r % 16 == 0 && nqr >= 1 && nqr <= 3 && (a.dim == 64 || a.dim == 128)) {
+    const int ipw = 8;
+    const dim3 grid((a.B_c + 4 * ipw - 1) / (4 * ipw)), block(256);
+    const int key = nqr * 8 + a.dim / 32;
+    switch (key) {
+      case 1 * 8 + 2: hipLaunchKernelGGL((fm_cand_kernel<1, 2>), grid, block, 0, s, a, ipw); break;
+      case 2 * 8 + 2: hipLaunchKernelGGL((fm_cand_kernel<2, 2>), grid, block, 0, s, a, ipw); break;
+      case 3 * 8 + 2: hipLaunchKernelGGL((fm_cand_kernel<3, 2>), grid, block, 0, s, a, ipw); break;
+      case 1 * 8 + 4: hipLaunchKernelGGL((fm_cand_kernel<1, 4>), grid, block, 0, s, a, ipw); break;
+      case 2 * 8 + 4: hipLaunchKernelGGL((fm_cand_kernel<2, 4>), grid, block, 0, s, a, ipw); break;
+      case 3 * 8 + 4: hipLaunchKernelGGL((fm_cand_kernel<3, 4>), grid, block, 0, s, a, ipw); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(fm_kernel_for(a.n_c, a.n_r + a.n_c, a.dim), dim3((a.B_c + 3) / 4), dim3(256), 0, s, a, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_token_lcb_request(const TokLcbArgs& a, hipStream_t s) {
   if (a.B_r <= 0) return hipSuccess;
+  // Matrix-core path: D a multiple of 32 up to 128, up to 128 output and 32
+  // input tokens, 8-byte aligned T_R rows.
+  const int T = a.t_r + a.t_c;
+  if (a.dim % 32 == 0 && a.dim <= 128 && T <= 128 && a.n_r <= 32 && (reinterpret_cast<uintptr_t>(a.y_r) & 7) == 0 &&
+      a.ldyr % 4 == 0 && (reinterpret_cast<uintptr_t>(a.z) & 15) == 0) {
+    const dim3 grid(a.B_r), block(64 * (a.dim / 32));
+    const int key = ((T + 31) / 32) * 4 + (a.n_r + 15) / 16;
+    switch (key) {
+      case 1 * 4 + 1: hipLaunchKernelGGL((tok_request_mfma_kernel<1, 1>), grid, block, 0, s, a); break;
+      case 1 * 4 + 2: hipLaunchKernelGGL((tok_request_mfma_kernel<1, 2>), grid, block, 0, s, a); break;
+      case 2 * 4 + 1: hipLaunchKernelGGL((tok_request_mfma_kernel<2, 1>), grid, block, 0, s, a); break;
+      case 2 * 4 + 2: hipLaunchKernelGGL((tok_request_mfma_kernel<2, 2>), grid, block, 0, s, a); break;
+      case 3 * 4 + 1: hipLaunchKernelGGL((tok_request_mfma_kernel<3, 1>), grid, block, 0, s, a); break;
+      case 3 * 4 + 2: hipLaunchKernelGGL((tok_request_mfma_kernel<3, 2>), grid, block, 0, s, a); break;
+      case 4 * 4 + 1: hipLaunchKernelGGL((tok_request_mfma_kernel<4, 1>), grid, block, 0, s, a); break;
+      case 4 * 4 + 2: hipLaunchKernelGGL((tok_request_mfma_kernel<4, 2>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const size_t lds = size_t(a.n_r) * a.dim * 2;
   hipLaunchKernelGGL(tok_request_kernel, dim3(a.B_r), dim3(256), lds, s, a);
   return hipGetLastError();

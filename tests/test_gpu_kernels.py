@@ -396,7 +396,9 @@ def test_encode_kv_parity():
 # ---------------------------------------------------------------- FM / token LCB
 
 
-@pytest.mark.parametrize("nr,nc,D", [(32, 16, 128),   # fixed-shape kernel, 1 x 3 blocks, 4 k-steps
+@pytest.mark.parametrize("nr,nc,D", [(32, 16, 128),   # request-caching candidate kernel, 4 k-steps
+                                     (16, 8, 64),     # request-caching kernel, padded candidate rows
+                                     (48, 16, 64),    # request-caching kernel, 3 request blocks
                                      (8, 4, 64),      # fixed-shape kernel, padded rows and columns
                                      (20, 12, 96),    # generic kernel (D not 32 * {2, 4})
                                      (40, 24, 64)])   # two row blocks for the request items
