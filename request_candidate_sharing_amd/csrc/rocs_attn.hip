@@ -2,23 +2,50 @@
 // IKBO-DCA): keys/values stay at request-batch size and every query tile is
 // made of queries of ONE request, so each staged key/value tile in LDS is
 // shared by all the queries of the workgroup, and the tiles of one request
-// run back to back on one XCD (shared L2).  The same kernel runs the
+// run back to back on one XCD (shared L2).  The same kernels run the
 // request-only encoder's self-attention (group = one request's sequence).
 //
 // Per workgroup: 4 waves x 32 queries = 128 queries of one group and one
-// head (head_dim 64).  Keys stream in 64-key slabs through double-buffered
-// LDS (K row-major, V transposed).  Each wave computes S^T = K Q^T with
+// head (head_dim 64).  Keys stream in 64-key slabs through LDS (K row-major,
+// V transposed).  Each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, so each lane holds scores of a single query:
-// the online-softmax max/sum need one cross-lane exchange (lane ^ 32) per
-// slab.  P^T is fed back as the B operand of O^T = V^T P^T in the register
-// order the S^T accumulator produced (the key order inside one MFMA k-step
-// only has to agree between the two operands).  Softmax in fp32 with exp2
-// and the scale folded into one multiply-add.
+// the online-softmax max/sum need one exchange between lanes l and l ^ 32
+// per slab (v_permlane32_swap).  P^T is fed back as the B operand of
+// O^T = V^T P^T in the register order the S^T accumulator produced (the key
+// order inside one MFMA k-step only has to agree between the two operands;
+// the V^T rows are stored in that order).  Softmax in fp32 with exp2 and the
+// scale folded into one multiply-add; the running maximum is only moved when
+// a score exceeds it by more than 2^8 in exp2 units (lazy rescaling).
+//
+// With V^T staged once per call (vtrans_kernel), attn_vt_kernel feeds K and
+// V^T slabs by LDS DMA through a 3-stage ring (two slabs in flight); without
+// it, attn_kernel stages through registers and transposes V into LDS.
 #include "rocs_device.h"
 
 namespace rocs {
 
 namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave-instruction of global -> LDS DMA: lane i's 16 bytes land at
+// dst + 16*i (dst wave-uniform).  Written as asm so that the compiler, which
+// would otherwise wait for every LDS DMA in flight before any LDS read, leaves
+// the ring's waits to the explicit vmcnt counts below.  No register receives
+// data (the load writes LDS only); the wait state after the M0 write is the
+// one LDS DMA needs.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const uint32_t m0 = uint32_t(uintptr_t((lds_ptr_t)dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt,
+// lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 constexpr int TQ = 128;  // queries per workgroup
 constexpr int KC = 64;   // keys per slab
@@ -26,14 +53,19 @@ constexpr int DH = 64;   // head dim
 
 // K tile: [64 keys][64 dh] bf16, 16-byte chunks swizzled by key.
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chunk ^ (key & 7)); }
-// V^T tile: [64 dh][64 keys] bf16 in 8-byte units (16 per row), swizzled by dh.
-__device__ __forceinline__ int vt_off(int dh, int unit) { return dh * 16 + (unit ^ (dh & 15)); }
+// V^T tile: [64 dh][64 keys] bf16, 16-byte chunks swizzled by dh.  Inside a row
+// the keys sit in the order the PV step consumes them: position = key with
+// bits 2 and 3 exchanged, so the 8 keys one lane feeds to one MFMA k-step
+// (two runs of 4 keys, 8 apart) are one 16-byte chunk.
+__device__ __forceinline__ int vt_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+__device__ __forceinline__ int vt_chunk(int dh, int chunk) { return dh * 8 + (chunk ^ (dh & 7)); }
 
-template <bool VT>
-__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
-  __shared__ uint4 sK[2][KC * 8];
-  __shared__ uint2 sV[2][DH * 16];
-
+// Query tile of one workgroup: group (request / sequence), rows [rbeg, rend)
+// of the query batch, head h.  Returns false when the workgroup has no tile.
+struct QTile {
+  int group, rbeg, rend, h;
+};
+__device__ __forceinline__ bool decode_tile(const AttnArgs& a, QTile& t) {
   const int H = a.n_heads;
   int n_tiles;
   if (a.q_rows_per_group > 0)
@@ -43,194 +75,302 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
   const int total = (a.q_rows_per_group > 0 ? n_tiles : a.max_tiles) * H;
   const int logical = xcd_remap(blockIdx.x, total);
   const int tile = logical / H;
-  const int h = logical - tile * H;
-  if (tile >= n_tiles) return;
-
-  int group, rbeg, rend;
+  t.h = logical - tile * H;
+  if (tile >= n_tiles) return false;
   if (a.q_rows_per_group > 0) {
     const int tpg = (a.q_rows_per_group + TQ - 1) / TQ;
-    group = tile / tpg;
-    rbeg = group * a.q_rows_per_group + (tile - group * tpg) * TQ;
-    rend = min(rbeg + TQ, (group + 1) * a.q_rows_per_group);
+    t.group = tile / tpg;
+    t.rbeg = t.group * a.q_rows_per_group + (tile - t.group * tpg) * TQ;
+    t.rend = min(t.rbeg + TQ, (t.group + 1) * a.q_rows_per_group);
   } else {
-    group = a.tile_info[3 * tile + 0];
-    rbeg = a.tile_info[3 * tile + 1];
-    rend = a.tile_info[3 * tile + 2];
+    t.group = a.tile_info[3 * tile + 0];
+    t.rbeg = a.tile_info[3 * tile + 1];
+    t.rend = a.tile_info[3 * tile + 2];
   }
+  return true;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5;  // half of the wave
-  const int q_local = rbeg + wave * 32 + (lane & 31);
-  const bool q_ok = q_local < rend;
-  const int64_t q_phys = q_ok ? (a.perm ? a.perm[q_local] : q_local) : 0;
-
-  if (group >= a.n_groups) {  // candidates whose request id was out of range
-    if (q_ok) {
-      bf16* o = a.o + q_phys * a.ldo + h * DH;
-      for (int e = hl * 32; e < hl * 32 + 32; ++e) o[e] = to_bf(nan_f());
-    }
-    return;
-  }
-
-  // Q^T fragments (B operand): lane holds query q_local, dh 16*ks + 8*hl + 0..7
+// Per-lane query state: the Q^T fragments (B operand; lane holds query
+// q_local, dh 16*ks + 8*hl + 0..7), the output accumulators O^T and the
+// online-softmax reference and sum.
+struct QState {
   bf16x8 qf[4];
-  {
-    const bf16* qp = a.q + q_phys * a.ldq + h * DH;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (q_ok) u = *reinterpret_cast<const uint4*>(qp + ks * 16 + hl * 8);
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  const bf16* kbase = a.k + int64_t(group) * a.kv_group_stride + h * DH;
-  const bf16* vbase = a.v + int64_t(group) * a.kv_group_stride + h * DH;
-  const bf16* vtbase = VT ? a.vt + (int64_t(group) * H + h) * DH * a.ldvt : nullptr;
-  const int L = a.L;
-  const int nslab = (L + KC - 1) / KC;
-
-  // each thread stages 2 K chunks and 2 V chunks (16 B) per slab
-  uint4 rk[2], rv[2];
-  auto gload = [&](int slab) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256;
-      const int key = id >> 3, c = id & 7;
-      const int gk = slab * KC + key;
-      rk[i] = gk < L ? *reinterpret_cast<const uint4*>(kbase + int64_t(gk) * a.ldkv + c * 8) : make_uint4(0, 0, 0, 0);
-      if constexpr (VT) {
-        // V^T row dh = id / 8, keys slab*64 + 8c .. +7 (padded with zeros up to ldvt)
-        rv[i] = *reinterpret_cast<const uint4*>(vtbase + int64_t(key) * a.ldvt + slab * KC + c * 8);
-      } else {
-        rv[i] = gk < L ? *reinterpret_cast<const uint4*>(vbase + int64_t(gk) * a.ldkv + c * 8) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256;
-      const int key = id >> 3, c = id & 7;
-      sK[buf][k_off(key, c)] = rk[i];
-      if constexpr (VT) {
-        // already transposed: row dh = id / 8 holds keys 8c .. 8c+7 = units 2c, 2c+1
-        sV[buf][vt_off(key, 2 * c)] = make_uint2(rv[i].x, rv[i].y);
-        sV[buf][vt_off(key, 2 * c + 1)] = make_uint2(rv[i].z, rv[i].w);
-      } else {
-        // transpose V: dh = c*8 + e, key -> unit key/4, lane-in-unit key%4
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rv[i]);
-        uint16_t* vt = reinterpret_cast<uint16_t*>(sV[buf]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dh = c * 8 + e;
-          vt[vt_off(dh, key >> 2) * 4 + (key & 3)] = e16[e];
-        }
-      }
-    }
-  };
-
   f32x16 o_acc[2];
+  float m_run, l_run;
+};
+
+// Candidates whose request id was out of range get NaN rows.
+__device__ __forceinline__ void write_nan_row(const AttnArgs& a, int64_t q_phys, int h, int hl) {
+  bf16* o = a.o + q_phys * a.ldo + h * DH;
+  for (int e = hl * 32; e < hl * 32 + 32; ++e) o[e] = to_bf(nan_f());
+}
+
+__device__ __forceinline__ void load_q(const AttnArgs& a, int64_t q_phys, bool q_ok, int h, int hl, QState& st) {
+  const bf16* qp = a.q + q_phys * a.ldq + h * DH;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (q_ok) u = *reinterpret_cast<const uint4*>(qp + ks * 16 + hl * 8);
+    st.qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o_acc[t][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.scale_log2;
+    for (int j = 0; j < 16; ++j) st.o_acc[t][j] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+}
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap gives every lane
+// both values: a VALU exchange, no LDS round trip).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-  for (int sb = 0; sb < nslab; ++sb) {
-    const int cur = sb & 1;
-    const bool more = sb + 1 < nslab;
-    if (more) gload(sb + 1);
-
-    // S^T tiles: keys kt*32 + row, queries = lane columns
-    f32x16 s[2];
+// One 64-key slab for the wave's 32 queries: S^T = K Q^T, online softmax,
+// O^T += V^T P^T.  tK: [64 keys][8 chunks] (k_off), tV: [64 dh][8 chunks]
+// (vt_chunk, keys in vt_pos order); key0 = first key of the slab.
+__device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, int key0, int L, float c, int lane,
+                                            QState& st) {
+  const int hl = lane >> 5;
+  // All 8 K fragments first (their LDS latency overlaps), then the S MFMAs.
+  uint4 kf[8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) kf[kt * 4 + ks] = tK[k_off(kt * 32 + (lane & 31), ks * 2 + hl)];
+  __builtin_amdgcn_sched_barrier(0);
+  // S^T tiles: keys kt*32 + row, queries = lane columns
+  f32x16 s[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 u = sK[cur][k_off(kt * 32 + (lane & 31), ks * 2 + hl)];
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[ks], s[kt], 0, 0, 0);
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kt * 4 + ks]), st.qf[ks], s[kt],
+                                                      0, 0, 0);
+  }
+  // V^T fragments next: read while the softmax below runs.
+  // keys kt*32 + 16*sp + 8*(q/4) + 4*hl + q%4 = chunk 4*kt + 2*sp + hl
+  uint4 vf[8];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) vf[dt * 4 + kt * 2 + sp] = tV[vt_chunk(dt * 32 + (lane & 31), 4 * kt + 2 * sp + hl)];
+  __builtin_amdgcn_sched_barrier(0);
+  // mask keys beyond L (last slab only)
+  if (key0 + KC > L) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = key0 + kt * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
+        if (key >= L) s[kt][j] = -INFINITY;
       }
-    }
-    // mask keys beyond L (last slab only)
-    if ((sb + 1) * KC > L) {
+  }
+  float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = sb * KC + kt * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-          if (key >= L) s[kt][j] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // v_exp_f32
-    const float mc = m_new * c;
-    float psum = 0.f;
-    bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][st * 8 + q], c, -mc));
-          psum += p;
-          pf[kt * 2 + st][q] = to_bf(p);
-        }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
+  mx = halves_max(mx);
+  // Lazy rescaling: the running reference m_run moves only when some query of
+  // the wave sees a score more than 2^8 above it (in exp2 units); otherwise
+  // P may reach 2^8, which fp32 sums and bf16 P hold as well as values <= 1.
+  // O and l always share one reference, so O / l is unchanged.
+  if (__builtin_amdgcn_ballot_w64((mx - st.m_run) * c > 8.f)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);  // 0 on the first slab
+    st.l_run *= alpha;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o_acc[t][j] *= alpha;
-
-    // O^T[dh][query] += V^T[dh][keys] P^T[keys][query]
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const int dh = dt * 32 + (lane & 31);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          // keys kt*32 + 16*st + 8*(q/4) + 4*hl + q%4 -> 8-byte units
-          const int u0 = (kt * 32 + 16 * st + 4 * hl) >> 2;
-          const uint2 lo = sV[cur][vt_off(dh, u0)];
-          const uint2 hi = sV[cur][vt_off(dh, u0 + 2)];
-          const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kt * 2 + st],
-                                                              o_acc[dt], 0, 0, 0);
-        }
-    }
-    if (more) sstore(cur ^ 1);
-    __syncthreads();
+      for (int j = 0; j < 16; ++j) st.o_acc[t][j] *= alpha;
+    st.m_run = m_new;
   }
+  const float mc = st.m_run * c;
+  float psum = 0.f;
+  bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pf[kt * 2 + sp][q] = to_bf(__builtin_amdgcn_exp2f(fmaf(s[kt][sp * 8 + q], c, -mc)));
+      // l sums the bf16 P the PV product uses, two at a time (v_dot2_f32_bf16 with ones)
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const bf16x2 pp = {pf[kt * 2 + sp][q], pf[kt * 2 + sp][q + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{to_bf(1.f), to_bf(1.f)}, psum, false);
+      }
+    }
+  psum = halves_sum(psum);
+  st.l_run += psum;
 
-  if (!q_ok) return;
-  const float inv = 1.0f / l_run;
+  // O^T[dh][query] += V^T[dh][keys] P^T[keys][query]
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
+        st.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[dt * 4 + kt * 2 + sp]),
+                                                               pf[kt * 2 + sp], st.o_acc[dt], 0, 0, 0);
+}
+
+__device__ __forceinline__ void write_out(const AttnArgs& a, int64_t q_phys, int h, int hl, const QState& st) {
+  const float inv = 1.0f / st.l_run;
   bf16* o = a.o + q_phys * a.ldo + h * DH;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // registers 4g..4g+3 hold dh = dt*32 + 8g + 4*hl + 0..3
-      bf16x4 pk = {to_bf(o_acc[dt][4 * g + 0] * inv), to_bf(o_acc[dt][4 * g + 1] * inv),
-                   to_bf(o_acc[dt][4 * g + 2] * inv), to_bf(o_acc[dt][4 * g + 3] * inv)};
+      bf16x4 pk = {to_bf(st.o_acc[dt][4 * g + 0] * inv), to_bf(st.o_acc[dt][4 * g + 1] * inv),
+                   to_bf(st.o_acc[dt][4 * g + 2] * inv), to_bf(st.o_acc[dt][4 * g + 3] * inv)};
       *reinterpret_cast<bf16x4*>(o + dt * 32 + 8 * g + 4 * hl) = pk;
     }
+}
+
+// V read row-major from the K/V rows and transposed into LDS on the way in
+// (register-staged, one slab ahead).
+__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
+  __shared__ uint4 sK[2][KC * 8];
+  __shared__ uint4 sV[2][DH * 8];
+  QTile t;
+  if (!decode_tile(a, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int q_local = t.rbeg + wave * 32 + (lane & 31);
+  const bool q_ok = q_local < t.rend;
+  const int64_t q_phys = q_ok ? (a.perm ? a.perm[q_local] : q_local) : 0;
+  if (t.group >= a.n_groups) {
+    if (q_ok) write_nan_row(a, q_phys, t.h, hl);
+    return;
+  }
+  QState st;
+  load_q(a, q_phys, q_ok, t.h, hl, st);
+  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH;
+  const bf16* vbase = a.v + int64_t(t.group) * a.kv_group_stride + t.h * DH;
+  const int L = a.L;
+  const int nslab = (L + KC - 1) / KC;
+
+  // each thread stages 2 K chunks and 2 V chunks (16 B) per slab; keys past L
+  // are zeros
+  uint4 rk[2], rv[2];
+  auto gload = [&](int slab) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + i * 256;
+      const int key = id >> 3, cc = id & 7;
+      const int gk = slab * KC + key;
+      rk[i] = gk < L ? *reinterpret_cast<const uint4*>(kbase + int64_t(gk) * a.ldkv + cc * 8) : make_uint4(0, 0, 0, 0);
+      rv[i] = gk < L ? *reinterpret_cast<const uint4*>(vbase + int64_t(gk) * a.ldkv + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + i * 256;
+      const int key = id >> 3, cc = id & 7;
+      sK[buf][k_off(key, cc)] = rk[i];
+      // transpose V: dh = cc*8 + e
+      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rv[i]);
+      uint16_t* vt = reinterpret_cast<uint16_t*>(sV[buf]);
+      const int pos = vt_pos(key);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dh = cc * 8 + e;
+        vt[vt_chunk(dh, pos >> 3) * 8 + (pos & 7)] = e16[e];
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int sb = 0; sb < nslab; ++sb) {
+    const int cur = sb & 1;
+    const bool more = sb + 1 < nslab;
+    if (more) gload(sb + 1);
+    attend_slab(sK[cur], sV[cur], sb * KC, L, a.scale_log2, lane, st);
+    if (more) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  if (q_ok) write_out(a, q_phys, t.h, hl, st);
+}
+
+// V^T staged by vtrans_kernel (rows of keys in vt_pos order, zero-padded to
+// a multiple of 64).  K and V^T slabs move global -> LDS by DMA
+// (global_load_lds_dwordx4) through a ring of NST stages, so two slabs are in
+// flight while one is consumed and no registers hold staged data.  Each wave
+// fills 2 of the 8 1-KB pieces of each tile; lane i fetches the 16-byte
+// chunk that the row swizzle places at its LDS slot.
+constexpr int NST = 3;
+constexpr int DMA_PER_SLAB = 4;  // wave-instructions per slab per wave (2 K + 2 V)
+
+__global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
+  __shared__ uint4 sK[NST][KC * 8];
+  __shared__ uint4 sV[NST][DH * 8];
+  QTile t;
+  if (!decode_tile(a, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q_local = t.rbeg + wave * 32 + (lane & 31);
+  const bool q_ok = q_local < t.rend;
+  const int64_t q_phys = q_ok ? (a.perm ? a.perm[q_local] : q_local) : 0;
+  if (t.group >= a.n_groups) {
+    if (q_ok) write_nan_row(a, q_phys, t.h, hl);
+    return;
+  }
+  const int L = a.L;
+  const int nslab = (L + KC - 1) / KC;
+
+  // LDS entry (2*wave + j)*64 + lane of a tile is row (2*wave + j)*8 + lane/8,
+  // slot lane%8, which holds global chunk (lane%8) ^ (row%8) of that row.
+  const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
+  const int row0 = wave * 16 + (lane >> 3);  // j = 0; j = 1 adds 8
+  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH + chunk * 8;
+  const bf16* vsrc = a.vt + ((int64_t(t.group) * a.n_heads + t.h) * DH + row0) * a.ldvt + chunk * 8;
+  const int64_t vstep = 8 * a.ldvt;
+  auto issue = [&](int slab, int stage) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // keys past L read row L-1: their scores are masked and their P is 0
+      const int key = min(slab * KC + row0 + 8 * j, L - 1);
+      dma16(kbase + int64_t(key) * a.ldkv, &sK[stage][(2 * wave + j) * 64]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(vsrc + j * vstep + slab * KC, &sV[stage][(2 * wave + j) * 64]);
+  };
+
+  // Every step issues one slab (the last one again once past the end), so
+  // "this wave's DMA for slab sb has landed" is always vmcnt <= one slab.
+  issue(0, 0);
+  issue(min(1, nslab - 1), 1);
+  QState st;
+  load_q(a, q_phys, q_ok, t.h, hl, st);
+  // The compiler does not see the DMA on the load counter: make it wait for
+  // the Q fragments here, once, rather than inside the loop at their first use.
+  asm volatile("" : : "v"(st.qf[0]), "v"(st.qf[1]), "v"(st.qf[2]), "v"(st.qf[3]));
+  int cur = 0, nxt = 2;
+  for (int sb = 0; sb < nslab; ++sb) {
+    wait_vmcnt<DMA_PER_SLAB>();
+    __syncthreads();  // slab sb is in LDS for all waves; stage nxt (slab sb-1) is free
+    issue(min(sb + 2, nslab - 1), nxt);
+    attend_slab(sK[cur], sV[cur], sb * KC, L, a.scale_log2, lane, st);
+    cur = cur == NST - 1 ? 0 : cur + 1;
+    nxt = nxt == NST - 1 ? 0 : nxt + 1;
+  }
+  wait_vmcnt<0>();  // no DMA may still write this workgroup's LDS when it exits
+  if (q_ok) write_out(a, q_phys, t.h, hl, st);
 }
 
 // ----------------------------------------------------------------- V^T staging
@@ -261,7 +401,8 @@ __global__ __launch_bounds__(256) void vtrans_kernel(const bf16* __restrict__ v,
     const int e = id >> 3, c = id & 7;
     uint32_t w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = uint32_t(t[c * 8 + 2 * j][e]) | (uint32_t(t[c * 8 + 2 * j + 1][e]) << 16);
+    for (int j = 0; j < 4; ++j)
+      w[j] = uint32_t(t[vt_pos(c * 8 + 2 * j)][e]) | (uint32_t(t[vt_pos(c * 8 + 2 * j + 1)][e]) << 16);
     *reinterpret_cast<uint4*>(vt + ((int64_t(g) * H + h) * DH + e) * Lp + kb * KC + c * 8) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -412,10 +553,11 @@ hipError_t launch_attn_plan(int B_r, int B_c, const int32_t* offsets, const int3
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int tiles = a.q_rows_per_group > 0 ? a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ) : a.max_tiles;
   if (tiles <= 0 || a.n_heads <= 0) return hipSuccess;
+  if (a.L <= 0) return hipErrorInvalidValue;
   if (a.vt != nullptr)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_vt_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

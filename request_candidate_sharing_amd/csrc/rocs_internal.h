@@ -101,7 +101,7 @@ struct AttnArgs {
   int64_t kv_group_stride;  // elements between groups (normally L*ldkv)
   bf16* o;
   int64_t ldo;
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e), > 0 (the lazy softmax rescaling relies on it)
   // grouping
   int n_groups;
   int q_rows_per_group;      // > 0: uniform groups, row r belongs to group r / q_rows_per_group
@@ -109,14 +109,15 @@ struct AttnArgs {
   const int32_t* n_tiles_dev;
   const int32_t* perm;  // optional row permutation: logical row r is physical row perm[r]
   int max_tiles;
-  // optional V^T staging (launch_vtrans): vt[((g*H + h)*64 + e)*ldvt + key]; when
-  // set, v/ldkv are not read for values
+  // optional V^T staging (launch_vtrans, layout below); when set, v is not read
   const bf16* vt;
   int64_t ldvt;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
-// V^T staging: vt[((g*H + h)*64 + e)*Lp + key] = v[g*gstride + key*ldv + h*64 + e] for
-// keys < L, 0 for L <= key < Lp = round_up(L, 64).
+// V^T staging: row (g*H + h)*64 + e of vt (Lp = round_up(L, 64) elements) holds
+// v[g*gstride + key*ldv + h*64 + e] for keys < L and 0 for L <= key < Lp, with
+// key at position 64*(key/64) + p(key%64), p exchanging bits 2 and 3 (the key
+// order the attention kernels' PV step consumes).
 hipError_t launch_vtrans(const bf16* v, int64_t ldv, int64_t gstride, int G, int H, int L, bf16* vt, hipStream_t s);
 inline int64_t vt_pad(int L) { return (int64_t(L) + 63) / 64 * 64; }
 int attn_tile_rows();

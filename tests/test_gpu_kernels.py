@@ -325,7 +325,7 @@ def test_validate_batch():
 # ---------------------------------------------------------------- attention
 
 
-def xattn_case(counts, L, H, seed, shuffle=False):
+def xattn_case(counts, L, H, seed, shuffle=False, kramp=None):
     R = _R()
     rng = np.random.default_rng(seed)
     d = H * 64
@@ -333,6 +333,10 @@ def xattn_case(counts, L, H, seed, shuffle=False):
     B, Bc = len(counts), sum(counts)
     q_r, q_c = rand(rng, (B, d), True), rand(rng, (Bc, d), True)
     kv = rand(rng, (B * L, 4 * d), True)  # [K_R | V_R | K_C | V_C] per token
+    if kramp is not None:  # per-key scale of the keys (both K_R and K_C)
+        f = np.tile(np.asarray(kramp, np.float64), B)[:, None]
+        kv[:, :d] = S.round_bf16(kv[:, :d] * f)
+        kv[:, 2 * d:3 * d] = S.round_bf16(kv[:, 2 * d:3 * d] * f)
     m = bt["cand2req"]
     perm = np.arange(Bc)
     if shuffle:
@@ -355,9 +359,24 @@ def xattn_case(counts, L, H, seed, shuffle=False):
 
 
 @pytest.mark.parametrize("counts,L,H", [([5, 0, 130, 300, 1], 200, 2), ([500, 499], 256, 4), ([1] * 7, 64, 1),
-                                        ([260, 3], 1024, 8)])
+                                        ([260, 3], 1024, 8), ([3, 70], 1, 2), ([129, 2], 65, 2), ([300], 333, 1),
+                                        ([40, 90], 129, 1)])
 def test_cross_attention_parity(counts, L, H):
     out = xattn_case(counts, L, H, seed=L + H)
+    assert rel_err(out["a_c"], out["ref_c"]) <= TOL_BF16
+    assert rel_err(out["a_r"], out["ref_r"]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("ramp", ["rising", "falling", "spike"])
+def test_cross_attention_wide_score_range(ramp):
+    """Scores that move by far more than 2^8 in exp2 units along the keys: a
+    running maximum that keeps rising (every later slab must rescale), one set
+    by the first slab (later P values are tiny), and a single dominant key
+    late in the sequence."""
+    L = 700
+    x = np.arange(L) / (L - 1)
+    kr = {"rising": 1.0 + 24.0 * x, "falling": 25.0 - 24.0 * x, "spike": np.where(np.arange(L) == 611, 40.0, 1.0)}
+    out = xattn_case([150, 7, 260], L, 2, seed=77, kramp=kr[ramp])
     assert rel_err(out["a_c"], out["ref_c"]) <= TOL_BF16
     assert rel_err(out["a_r"], out["ref_r"]) <= TOL_BF16
 
