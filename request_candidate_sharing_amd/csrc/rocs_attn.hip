@@ -51,14 +51,19 @@ constexpr int TQ = 128;  // queries per workgroup
 constexpr int KC = 64;   // keys per slab
 constexpr int DH = 64;   // head dim
 
-// K tile: [64 keys][64 dh] bf16, 16-byte chunks swizzled by key.
-__device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chunk ^ (key & 7)); }
-// V^T tile: [64 dh][64 keys] bf16, 16-byte chunks swizzled by dh.  Inside a row
-// the keys sit in the order the PV step consumes them: position = key with
-// bits 2 and 3 exchanged, so the 8 keys one lane feeds to one MFMA k-step
-// (two runs of 4 keys, 8 apart) are one 16-byte chunk.
+// Tiles hold 8 16-byte chunks per 128-byte row; chunk c of row r sits at
+// c ^ swz(r).  A fragment read (32 consecutive rows, one chunk column) then
+// hits distinct banks in every group of 16 lanes (256 B of banks per clock),
+// and in every group of 8.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// K tile: [64 keys][64 dh] bf16.
+__device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chunk ^ swz(key)); }
+// V^T tile: [64 dh][64 keys] bf16.  Inside a row the keys sit in the order
+// the PV step consumes them: position = key with bits 2 and 3 exchanged, so
+// the 8 keys one lane feeds to one MFMA k-step (two runs of 4 keys, 8 apart)
+// are one 16-byte chunk.
 __device__ __forceinline__ int vt_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
-__device__ __forceinline__ int vt_chunk(int dh, int chunk) { return dh * 8 + (chunk ^ (dh & 7)); }
+__device__ __forceinline__ int vt_chunk(int dh, int chunk) { return dh * 8 + (chunk ^ swz(dh)); }
 
 // Query tile of one workgroup: group (request / sequence), rows [rbeg, rend)
 // of the query batch, head h.  Returns false when the workgroup has no tile.
@@ -333,22 +338,24 @@ __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
   const int L = a.L;
   const int nslab = (L + KC - 1) / KC;
 
-  // LDS entry (2*wave + j)*64 + lane of a tile is row (2*wave + j)*8 + lane/8,
-  // slot lane%8, which holds global chunk (lane%8) ^ (row%8) of that row.
-  const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
+  // LDS entry (2*wave + j)*64 + lane of a tile is row r = (2*wave + j)*8 +
+  // lane/8, slot lane%8, which holds global chunk (lane%8) ^ swz(r) of that
+  // row; swz(r) = (lane/8) ^ j.
   const int row0 = wave * 16 + (lane >> 3);  // j = 0; j = 1 adds 8
-  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH + chunk * 8;
-  const bf16* vsrc = a.vt + ((int64_t(t.group) * a.n_heads + t.h) * DH + row0) * a.ldvt + chunk * 8;
+  const int chunk0 = (lane & 7) ^ ((lane >> 3) & 7);
+  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH;
+  const bf16* vsrc = a.vt + ((int64_t(t.group) * a.n_heads + t.h) * DH + row0) * a.ldvt;
   const int64_t vstep = 8 * a.ldvt;
   auto issue = [&](int slab, int stage) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       // keys past L read row L-1: their scores are masked and their P is 0
       const int key = min(slab * KC + row0 + 8 * j, L - 1);
-      dma16(kbase + int64_t(key) * a.ldkv, &sK[stage][(2 * wave + j) * 64]);
+      dma16(kbase + int64_t(key) * a.ldkv + (chunk0 ^ j) * 8, &sK[stage][(2 * wave + j) * 64]);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(vsrc + j * vstep + slab * KC, &sV[stage][(2 * wave + j) * 64]);
+    for (int j = 0; j < 2; ++j)
+      dma16(vsrc + j * vstep + slab * KC + (chunk0 ^ j) * 8, &sV[stage][(2 * wave + j) * 64]);
   };
 
   // Every step issues one slab (the last one again once past the end), so
