@@ -218,6 +218,56 @@ def other_workload(args):
     print(json.dumps(out), flush=True)
 
 
+def regime_study(args):
+    """Shared vs dense-broadcast step time on the GLM MLP stack shapes with a
+    fixed number of candidates per request, N in {1, 10, 100, 500, 1000}
+    (256 requests): the regime in which request sharing pays, and the
+    N = 500 ratio check."""
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    cfg = S.config(2)
+    for n in (1, 10, 100, 500, 1000):
+        inp = S.make_inputs(cfg, counts=[n] * cfg.B)
+        B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+        st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+        t_sh, _ = time_steps(st.run, args.steps, args.warmup)
+        del st
+        de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+        t_de, _ = time_steps(de.run, args.steps, args.warmup)
+        del de
+        F, _ = glm_mlp_work(cfg, B_r, B_c)
+        sh = t_sh / args.steps
+        print(json.dumps({"study": "regime", "workload": 2, "n_per_request": n, "B_r": B_r, "B_c": B_c,
+                          "shared_ms": sh * 1e3, "dense_broadcast_ms": t_de / args.steps * 1e3,
+                          "speedup_vs_dense_broadcast": t_de / t_sh, "candidates_per_s": B_c / sh,
+                          "mfma_util_pct": 100.0 * F / sh / PEAK_BF16}), flush=True)
+
+
+def order_study(args):
+    """Shared step time with candidates contiguous per request (offsets given)
+    and in a random global order (offsets NULL: the kernels resolve
+    cand2req row by row and the attention plan sorts candidates on the
+    device)."""
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    for k in (2, 3, 4, 5):
+        cfg = S.config(k)
+        inp = S.make_inputs(cfg)
+        res = {}
+        for name, data in (("contiguous", inp), ("shuffled", S.shuffle_candidates(inp))):
+            st = DeviceStack(data, mode=R.ROCS_EXEC_SHARED)
+            t, _ = time_steps(st.run, args.steps, args.warmup)
+            del st
+            res[name] = t / args.steps * 1e3
+        print(json.dumps({"study": "candidate_order", "workload": k, "B_r": cfg.B, "B_c": int(len(inp["cand2req"])),
+                          "contiguous_ms": res["contiguous"], "shuffled_ms": res["shuffled"],
+                          "shuffled_over_contiguous": res["shuffled"] / res["contiguous"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +280,10 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
     ap.add_argument("--workload", type=int, default=2,
                     help="profiling aid: time another workload's stack (1-5); the benchmark line is workload 2")
+    ap.add_argument("--regime", action="store_true",
+                    help="study: shared vs dense broadcast at N = 1..1000 candidates per request (workload 2 shapes)")
+    ap.add_argument("--order", action="store_true",
+                    help="study: contiguous vs shuffled candidate order on workloads 2-5")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -249,6 +303,10 @@ def main():
     from request_candidate_sharing_amd.stacks import DeviceStack
 
     torch.cuda.set_device(0)
+    if args.regime:
+        return regime_study(args)
+    if args.order:
+        return order_study(args)
     if args.workload != 2:
         return other_workload(args)
     cfg = S.config(2)
