@@ -203,8 +203,10 @@ def other_workload(args):
 
     cfg = S.config(args.workload)
     inp = S.make_inputs(cfg)
+    if args.shuffle:
+        inp = S.shuffle_candidates(inp)
     B_r, B_c = cfg.B, int(len(inp["cand2req"]))
-    log(f"bench: workload {args.workload} ({cfg.name()}) B_r={B_r} B_c={B_c}")
+    log(f"bench: workload {args.workload} ({cfg.name()}) B_r={B_r} B_c={B_c}" + (" shuffled" if args.shuffle else ""))
     st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
     t_sh, _ = time_steps(st.run, args.steps, args.warmup)
     del st
@@ -284,6 +286,8 @@ def main():
                     help="study: shared vs dense broadcast at N = 1..1000 candidates per request (workload 2 shapes)")
     ap.add_argument("--order", action="store_true",
                     help="study: contiguous vs shuffled candidate order on workloads 2-5")
+    ap.add_argument("--shuffle", action="store_true",
+                    help="with --workload k (k != 2): candidates in one random global order (offsets NULL)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

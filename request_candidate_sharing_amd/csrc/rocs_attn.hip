@@ -466,6 +466,67 @@ __global__ void plan_scatter(const int32_t* cand2req, int B_c, int B_r, int32_t*
   perm[atomicAdd(&cursor[m], 1)] = i;
 }
 
+// The same counting sort with the counts privatized per workgroup in LDS
+// (up to PLAN_LDS_BUCKETS buckets): one global atomic per (workgroup,
+// bucket present) instead of one per candidate, which serializes hundreds of
+// candidates of one request on one counter.  The order of a request's
+// candidates within its bucket is the order the atomics happen to run in;
+// the attention of one query does not depend on it.
+constexpr int PLAN_IT = 4;                // candidates per thread
+constexpr int PLAN_LDS_BUCKETS = 8000;    // B_r + 1 limit of the LDS path (the scatter holds 2 ints per bucket)
+
+__global__ __launch_bounds__(256) void plan_hist_lds(const int32_t* cand2req, int B_c, int B_r, int32_t* cnt) {
+  extern __shared__ int32_t h[];  // [B_r + 1]
+  const int nb = B_r + 1;
+  for (int b = threadIdx.x; b < nb; b += 256) h[b] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * 256 * PLAN_IT;
+#pragma unroll
+  for (int k = 0; k < PLAN_IT; ++k) {
+    const int i = base + k * 256 + threadIdx.x;
+    if (i < B_c) {
+      int m = cand2req[i];
+      if ((unsigned)m >= (unsigned)B_r) m = B_r;
+      atomicAdd(&h[m], 1);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += 256)
+    if (h[b]) atomicAdd(&cnt[b], h[b]);
+}
+
+__global__ __launch_bounds__(256) void plan_scatter_lds(const int32_t* cand2req, int B_c, int B_r, int32_t* cursor,
+                                                        int32_t* perm) {
+  extern __shared__ int32_t h[];  // [B_r + 1] local counts, then local cursors; [B_r + 1] bases
+  const int nb = B_r + 1;
+  int32_t* first = h + nb;
+  for (int b = threadIdx.x; b < nb; b += 256) h[b] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * 256 * PLAN_IT;
+  int mk[PLAN_IT];
+#pragma unroll
+  for (int k = 0; k < PLAN_IT; ++k) {
+    const int i = base + k * 256 + threadIdx.x;
+    mk[k] = -1;
+    if (i < B_c) {
+      int m = cand2req[i];
+      if ((unsigned)m >= (unsigned)B_r) m = B_r;
+      mk[k] = m;
+      atomicAdd(&h[m], 1);
+    }
+  }
+  __syncthreads();
+  // reserve this workgroup's range in every bucket it touches
+  for (int b = threadIdx.x; b < nb; b += 256) {
+    if (h[b]) first[b] = atomicAdd(&cursor[b], h[b]);
+    h[b] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PLAN_IT; ++k)
+    if (mk[k] >= 0) perm[first[mk[k]] + atomicAdd(&h[mk[k]], 1)] = base + k * 256 + threadIdx.x;
+}
+
 // Single workgroup: prefix sums over requests and the tile table.
 // offsets_in (nullable): contiguous batch; otherwise counts in cnt.
 __global__ __launch_bounds__(1024) void plan_tiles(const int32_t* offsets_in, int B_r, int B_c, PlanWs w) {
@@ -548,12 +609,24 @@ hipError_t launch_attn_plan(int B_r, int B_c, const int32_t* offsets, const int3
     return hipGetLastError();
   }
   *perm = w.perm;
+  const bool lds = B_r + 1 <= PLAN_LDS_BUCKETS;
+  const int g = (B_c + 256 * PLAN_IT - 1) / (256 * PLAN_IT);
+  const size_t hb = size_t(B_r + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(plan_clear, dim3((B_r + 2 + 255) / 256), dim3(256), 0, s, w.cnt, B_r + 2);
-  if (B_c > 0) hipLaunchKernelGGL(plan_hist, dim3((B_c + 255) / 256), dim3(256), 0, s, cand2req, B_c, B_r, w.cnt);
+  if (B_c > 0) {
+    if (lds)
+      hipLaunchKernelGGL(plan_hist_lds, dim3(g), dim3(256), hb, s, cand2req, B_c, B_r, w.cnt);
+    else
+      hipLaunchKernelGGL(plan_hist, dim3((B_c + 255) / 256), dim3(256), 0, s, cand2req, B_c, B_r, w.cnt);
+  }
   hipLaunchKernelGGL(plan_tiles, dim3(1), dim3(1024), 0, s, nullptr, B_r, B_c, w);
-  if (B_c > 0)
-    hipLaunchKernelGGL(plan_scatter, dim3((B_c + 255) / 256), dim3(256), 0, s, cand2req, B_c, B_r, w.cursor,
-                       w.perm);
+  if (B_c > 0) {
+    if (lds)
+      hipLaunchKernelGGL(plan_scatter_lds, dim3(g), dim3(256), 2 * hb, s, cand2req, B_c, B_r, w.cursor, w.perm);
+    else
+      hipLaunchKernelGGL(plan_scatter, dim3((B_c + 255) / 256), dim3(256), 0, s, cand2req, B_c, B_r, w.cursor,
+                         w.perm);
+  }
   return hipGetLastError();
 }
 
