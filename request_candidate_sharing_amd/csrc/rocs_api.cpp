@@ -200,10 +200,9 @@ int lcb_candidate_check(const rocs_batch* batch, rocs_dtype dt, const void* x_c,
 }
 
 // zmap == nullptr: z holds one row per candidate (dense-broadcast comparator).
-int lcb_candidate_launch(int B_c, int B_r, const int32_t* zmap, rocs_dtype dt, const void* x_c, int64_t ld_xc,
-                         int32_t d_in_c, const void* w_cc, const void* b_c, int32_t d_out_c, int act, const float* z,
-                         int64_t ld_z, const void* res_c, int64_t ld_resc, void* y_c, int64_t ld_yc, hipStream_t s) {
-  if (B_c == 0 || d_out_c == 0) return ROCS_OK;
+GemmArgs lcb_candidate_args(int B_c, int B_r, const int32_t* zmap, const void* x_c, int64_t ld_xc, int32_t d_in_c,
+                            const void* w_cc, const void* b_c, int32_t d_out_c, int act, const float* z, int64_t ld_z,
+                            const void* res_c, int64_t ld_resc, void* y_c, int64_t ld_yc) {
   GemmArgs g{};
   g.M = B_c;
   g.N = d_out_c;
@@ -225,6 +224,15 @@ int lcb_candidate_launch(int B_c, int B_r, const int32_t* zmap, rocs_dtype dt, c
   g.act = act;
   g.res = res_c;
   g.ldres = ld_resc;
+  return g;
+}
+
+int lcb_candidate_launch(int B_c, int B_r, const int32_t* zmap, rocs_dtype dt, const void* x_c, int64_t ld_xc,
+                         int32_t d_in_c, const void* w_cc, const void* b_c, int32_t d_out_c, int act, const float* z,
+                         int64_t ld_z, const void* res_c, int64_t ld_resc, void* y_c, int64_t ld_yc, hipStream_t s) {
+  if (B_c == 0 || d_out_c == 0) return ROCS_OK;
+  const GemmArgs g = lcb_candidate_args(B_c, B_r, zmap, x_c, ld_xc, d_in_c, w_cc, b_c, d_out_c, act, z, ld_z, res_c,
+                                        ld_resc, y_c, ld_yc);
   ROCS_HIP(launch_gemm(DType(dt), g, s), "rocs_lcb_candidate");
   return ROCS_OK;
 }

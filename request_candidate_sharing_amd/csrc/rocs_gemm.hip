@@ -175,6 +175,7 @@ enum : int {
   EPI_BIAS = 2,
   EPI_RELU = 4,
   EPI_RES = 8,
+  EPI_ZACC = 16,  // with EPI_Z: the tile's accumulators started at Z[m_i] (zinit_acc)
 };
 
 // Writes one 32-row block-row of a wave's tile through the epilogue.  Block
@@ -200,8 +201,8 @@ __device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, i
   const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
   const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
   bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
-  const bool has_z = ANY ? z != nullptr : (EPI & EPI_Z) != 0;
-  const bool has_map = ANY ? a.zmap != nullptr : (EPI & EPI_Z) != 0;
+  const bool has_z = ANY ? z != nullptr : (EPI & EPI_Z) != 0 && (EPI & EPI_ZACC) == 0;
+  const bool has_map = ANY ? a.zmap != nullptr : (EPI & EPI_Z) != 0 && (EPI & EPI_ZACC) == 0;
   const bool has_bias = ANY ? bias != nullptr : (EPI & EPI_BIAS) != 0;
   const bool relu = ANY ? a.act == 1 : (EPI & EPI_RELU) != 0;
   const bool has_res = ANY ? res != nullptr : (EPI & EPI_RES) != 0;
@@ -330,11 +331,16 @@ __device__ __forceinline__ void store_blocks_as(const GemmArgs& a, int mb, int n
 template <int JWM = 2, int FM, int FN>
 __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, const f32x16 (&acc)[FM][FN],
                                              float* stage) {
+  constexpr int ZA = EPI_Z | EPI_ZACC;
   switch (a.epi) {
     case EPI_Z | EPI_BIAS | EPI_RELU: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
     case EPI_Z | EPI_BIAS | EPI_RES: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
     case EPI_Z | EPI_RELU: store_blocks_as<EPI_Z | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
     case EPI_Z | EPI_RES: store_blocks_as<EPI_Z | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
+    case ZA | EPI_BIAS | EPI_RELU: store_blocks_as<ZA | EPI_BIAS | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
+    case ZA | EPI_BIAS | EPI_RES: store_blocks_as<ZA | EPI_BIAS | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
+    case ZA | EPI_RELU: store_blocks_as<ZA | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
+    case ZA | EPI_RES: store_blocks_as<ZA | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
     default: store_blocks_as<EPI_ANY, JWM>(a, mb, nb, lane, acc, stage); break;
   }
 }
@@ -422,6 +428,35 @@ __device__ __forceinline__ const void* pinned_zero_page() {
   return zero;
 }
 
+// Starts a wave's accumulators at the request contribution Z[m_i] of its
+// rows (EPI_ZACC launches), so the epilogue has nothing left to gather and
+// the Z loads overlap the first slab's DMA: acc = Z[m] + the products, in
+// that order.  A row whose map entry is out of range starts at NaN.  Block
+// (i, j): lane holds row mb + 32i + lane%32 and columns nb + 32j + 8g +
+// 4*(lane/32) + 0..3 in registers 4g..4g+3.  Offsets are 32-bit (checked
+// when the variant is chosen).
+template <int FM, int FN>
+__device__ __forceinline__ void zinit_acc(const GemmArgs& a, int mb, int nb, int lane, f32x16 (&acc)[FM][FN]) {
+  const int hk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = min(mb + i * 32 + (lane & 31), a.M - 1);
+    const int zr = a.zmap ? a.zmap[row] : row;  // no map: Z has one row per output row
+    const bool bad = (unsigned)zr >= (unsigned)a.zrows;
+    const float* zp = a.z + (uint32_t(bad ? 0 : zr) * uint32_t(a.ldz) + uint32_t(nb + 4 * hk));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = *reinterpret_cast<const float4*>(zp + j * 32 + 8 * g);
+        acc[i][j][4 * g + 0] = bad ? nan_f() : v.x;
+        acc[i][j][4 * g + 1] = bad ? nan_f() : v.y;
+        acc[i][j][4 * g + 2] = bad ? nan_f() : v.z;
+        acc[i][j][4 * g + 3] = bad ? nan_f() : v.w;
+      }
+  }
+}
+
 // One BM x BN output tile at (m0, n0) on a workgroup of WM x WN waves, with
 // the ring (NS slots of BM + BN rows of one 64-wide slab) at smem; slab kb
 // lives in slot kb % NS.
@@ -445,12 +480,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uin
   Feed feed;
   feed.init(a, ws, m0, n0, wave, lane);
   f32x16 acc[FM][FN];
-  zero_acc(acc);
 
   const int nk = (a.K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) feed.issue(a.K, zero, s * BK, slot(s), wave);
+  if (a.epi & EPI_ZACC)
+    zinit_acc(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
+  else
+    zero_acc(acc);
 
   const int xr0 = wm * WTM + (lane & 31);
   const int wr0 = BM + wn * WTN + (lane & 31);
@@ -563,7 +601,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a) {
     for (int w = 1; w < SPLIT; ++w) v += part[(w * 16 + r) * 64 + lane];
     acc[0][0][r] = v;
   }
-  store_blocks(a, m0, n0, lane, acc, part + SPLIT * 16 * 64);
+  // The partial sums started at zero, so the epilogue adds Z: the mapped
+  // variant without EPI_ZACC, or the generic one when Z has no map (only
+  // EPI_ZACC variants accept an unmapped Z).
+  GemmArgs e = a;
+  if (e.epi & EPI_ZACC) e.epi = a.zmap ? (e.epi & ~EPI_ZACC) : EPI_ANY;
+  store_blocks(e, m0, n0, lane, acc, part + SPLIT * 16 * 64);
 }
 
 // fp32 path: LDS-tiled SIMT GEMM, 64 x 64 tile, each thread 4 x 4 outputs,
@@ -690,21 +733,29 @@ hipError_t launch_mixed(const GemmArgs& a, int M1, int h2, int grid, hipStream_t
 // Epilogue variant of a launch: one of the specialised ones when the terms
 // match and every offset fits 32 bits, else EPI_ANY.
 int epilogue_variant(const GemmArgs& a) {
-  if (a.z == nullptr || a.zmap == nullptr || a.out0_f32 || a.act > 1) return EPI_ANY;
+  if (a.z == nullptr || a.out0_f32 || a.act > 1) return EPI_ANY;
   const int64_t lim = int64_t(1) << 31;
   if (int64_t(a.zrows) * a.ldz >= lim || int64_t(a.M) * a.ld0 >= lim) return EPI_ANY;
   if (a.res != nullptr && int64_t(a.M) * a.ldres >= lim) return EPI_ANY;
+  // Z goes into the accumulators at tile start when no tile takes the edge
+  // path (which adds Z itself): N a multiple of every tile width, one output.
+  // Mapped and unmapped Z (the dense-broadcast comparator's copied rows) then
+  // sum in the same order.
+  const bool zacc = a.N % 256 == 0 && a.n_split >= a.N;
+  if (a.zmap == nullptr && !zacc) return EPI_ANY;
   const int v = EPI_Z | (a.bias ? EPI_BIAS : 0) | (a.act == 1 ? EPI_RELU : 0) | (a.res ? EPI_RES : 0);
   switch (v) {
     case EPI_Z | EPI_BIAS | EPI_RELU:
     case EPI_Z | EPI_BIAS | EPI_RES:
     case EPI_Z | EPI_RELU:
     case EPI_Z | EPI_RES:
-      return v;
+      return zacc ? v | EPI_ZACC : v;
     default:
       return EPI_ANY;
   }
 }
+
+bool gemm_z_in_accumulators(const GemmArgs& a) { return (epilogue_variant(a) & EPI_ZACC) != 0; }
 
 hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   GemmArgs a = args;

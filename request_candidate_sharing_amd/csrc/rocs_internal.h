@@ -49,6 +49,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
+// Whether launch_gemm sums this launch as Z + products (accumulators started
+// at the gathered Z rows) rather than products + Z.
+bool gemm_z_in_accumulators(const GemmArgs& a);
 
 // y = act(norm(x + res) * gamma + beta) on rows of width w (one launch per group).
 struct NormArgs {
@@ -181,6 +184,9 @@ struct MlpArgs {
   int act2;
   const int32_t* zmap;  // null: Z rows are candidate rows
   int zrows;
+  // 1: accumulate onto Z (Z + products), the order the unfused candidate GEMM
+  // uses for the same layer (gemm_z_in_accumulators); 0: add Z at the end
+  int z1_first, z2_first;
   int residual;  // add x (d_in == d_out)
   int norm;      // -1 none, 0 LayerNorm, 1 RMSNorm (statistics over d_out)
   float eps;

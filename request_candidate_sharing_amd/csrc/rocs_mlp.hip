@@ -33,7 +33,7 @@ constexpr int HC = 128;       // hidden chunk
 constexpr int NT = 256;       // threads per workgroup
 constexpr int SLAB_U4 = 4096; // 64 KB slab in uint4
 
-template <int FNB>
+template <int FNB, bool Z2F>
 __global__ __launch_bounds__(NT, 1) void mlp_block_kernel(MlpArgs a) {
   __shared__ uint4 ring[2][SLAB_U4];  // 128 KB
   __shared__ uint4 hs[BM * HC / 8];   // 32 KB: hidden chunk, 16 chunks per row
@@ -99,7 +99,27 @@ __global__ __launch_bounds__(NT, 1) void mlp_block_kernel(MlpArgs a) {
   }
 
   f32x16 oacc[2][FNB];
-  zero_acc(oacc);
+  if constexpr (Z2F) {
+    // the second GEMM accumulates onto Z2 (blocks past d_out start at 0)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < FNB; ++j) {
+        const int cb = (wn * FNB + j) * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 zz = cb < a.d_out
+                                ? *reinterpret_cast<const float4*>(a.z2 + int64_t(zr[i]) * a.ldz2 + cb + 8 * g + 4 * hk)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          oacc[i][j][4 * g + 0] = zz.x;
+          oacc[i][j][4 * g + 1] = zz.y;
+          oacc[i][j][4 * g + 2] = zz.z;
+          oacc[i][j][4 * g + 3] = zz.w;
+        }
+      }
+  } else {
+    zero_acc(oacc);
+  }
 
   int st = 0;
   issue_a(0, 0, 0);
@@ -121,9 +141,20 @@ __global__ __launch_bounds__(NT, 1) void mlp_block_kernel(MlpArgs a) {
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 
-    // first GEMM: hacc = x W1_chunk^T
+    // first GEMM: hacc = x W1_chunk^T (onto Z1 when z1_first)
     f32x16 hacc[2][2];
-    zero_acc(hacc);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 zi = a.z1_first ? z1v[i][j][g] : make_float4(0.f, 0.f, 0.f, 0.f);
+          hacc[i][j][4 * g + 0] = zi.x;
+          hacc[i][j][4 * g + 1] = zi.y;
+          hacc[i][j][4 * g + 2] = zi.z;
+          hacc[i][j][4 * g + 3] = zi.w;
+        }
     for (int k = 0; k < nA; ++k) {
       if (k + 1 < nA)
         issue_a(c, k + 1, st ^ 1);
@@ -144,8 +175,13 @@ __global__ __launch_bounds__(NT, 1) void mlp_block_kernel(MlpArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = wn * 64 + j * 32 + 8 * g + 4 * hk;
-          float v[4] = {hacc[i][j][4 * g] + z1v[i][j][g].x, hacc[i][j][4 * g + 1] + z1v[i][j][g].y,
-                        hacc[i][j][4 * g + 2] + z1v[i][j][g].z, hacc[i][j][4 * g + 3] + z1v[i][j][g].w};
+          float v[4] = {hacc[i][j][4 * g], hacc[i][j][4 * g + 1], hacc[i][j][4 * g + 2], hacc[i][j][4 * g + 3]};
+          if (!a.z1_first) {
+            v[0] += z1v[i][j][g].x;
+            v[1] += z1v[i][j][g].y;
+            v[2] += z1v[i][j][g].z;
+            v[3] += z1v[i][j][g].w;
+          }
           if (col < hw) {
             if (a.b1) {
               const bf16x4 bb = *reinterpret_cast<const bf16x4*>(a.b1 + c * HC + col);
@@ -211,9 +247,14 @@ __global__ __launch_bounds__(NT, 1) void mlp_block_kernel(MlpArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = (valid ? cb : 0) + 8 * g + 4 * hk;
-        const float4 zz = *reinterpret_cast<const float4*>(a.z2 + int64_t(zr[i]) * a.ldz2 + col);
-        float v[4] = {oacc[i][j][4 * g] + zz.x, oacc[i][j][4 * g + 1] + zz.y, oacc[i][j][4 * g + 2] + zz.z,
-                      oacc[i][j][4 * g + 3] + zz.w};
+        float v[4] = {oacc[i][j][4 * g], oacc[i][j][4 * g + 1], oacc[i][j][4 * g + 2], oacc[i][j][4 * g + 3]};
+        if constexpr (!Z2F) {
+          const float4 zz = *reinterpret_cast<const float4*>(a.z2 + int64_t(zr[i]) * a.ldz2 + col);
+          v[0] += zz.x;
+          v[1] += zz.y;
+          v[2] += zz.z;
+          v[3] += zz.w;
+        }
         if (a.b2) {
           const bf16x4 bb = *reinterpret_cast<const bf16x4*>(a.b2 + col);
 #pragma unroll
@@ -344,12 +385,25 @@ hipError_t launch_mlp_block(const MlpArgs& a, hipStream_t s) {
   if (!mlp_block_supported(a.d_in, a.hidden, a.d_out) || (a.residual && a.d_in != a.d_out))
     return hipErrorInvalidValue;
   const int ntiles = (a.M + BM - 1) / BM;
-  if (a.d_out <= 128)
-    hipLaunchKernelGGL(mlp_block_kernel<2>, dim3(ntiles), dim3(NT), 0, s, a);
-  else if (a.d_out <= 256)
-    hipLaunchKernelGGL(mlp_block_kernel<4>, dim3(ntiles), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(mlp_block_kernel<8>, dim3(ntiles), dim3(NT), 0, s, a);
+  // Z2 summed first or last is fixed per launch: a template parameter keeps
+  // the unused path out of the register allocation
+  if (a.d_out <= 128) {
+    if (a.z2_first)
+      hipLaunchKernelGGL((mlp_block_kernel<2, true>), dim3(ntiles), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((mlp_block_kernel<2, false>), dim3(ntiles), dim3(NT), 0, s, a);
+  } else if (a.d_out <= 256) {
+    if (a.z2_first)
+      hipLaunchKernelGGL((mlp_block_kernel<4, true>), dim3(ntiles), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((mlp_block_kernel<4, false>), dim3(ntiles), dim3(NT), 0, s, a);
+  } else {
+    // 256 accumulators per lane leave no registers to start them at Z2: Z2 is
+    // added last here, so with d_out > 256 the fused block and the unfused
+    // layers agree to rounding rather than bit for bit when the unfused GEMM
+    // sums Z first
+    hipLaunchKernelGGL((mlp_block_kernel<8, false>), dim3(ntiles), dim3(NT), 0, s, a);
+  }
   return hipGetLastError();
 }
 
