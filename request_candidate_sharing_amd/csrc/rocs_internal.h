@@ -67,6 +67,17 @@ struct NormArgs {
   float eps;
   int act;
   int64_t ldres;  // 0: same as ldx
+  // Optional score head on the rounded output rows, with launch_rowdot's
+  // arithmetic and order (same bits): head_out[i] = head_w . y[i]
+  // (+ head_z[head_zmap[i]], NaN for a map entry out of range) + head_bias
+  // (+ head_bias_dev[0]).  head_w null: no head.
+  const void* head_w;
+  const float* head_z;
+  const int32_t* head_zmap;
+  int head_zrows;
+  float head_bias;
+  const void* head_bias_dev;
+  float* head_out;
 };
 hipError_t launch_norm(DType dt, const NormArgs& a, hipStream_t s);
 

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   }
   const T* g = reinterpret_cast<const T*>(a.gamma);
   const T* b = reinterpret_cast<const T*>(a.beta);
+  const T* hw = reinterpret_cast<const T*>(a.head_w);
   T* y = reinterpret_cast<T*>(a.y) + int64_t(row) * a.ldy;
+  float hs = 0.f;  // fused head: the same chunks and order as rowdot_kernel
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int e0 = (c * 64 + lane) * VEC;
@@ -82,9 +84,29 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
     }
     if (e0 + VEC <= a.width) {
       *reinterpret_cast<uint4*>(y + e0) = *reinterpret_cast<const uint4*>(out);
+      if (hw) {
+        const uint4 uw = *reinterpret_cast<const uint4*>(hw + e0);
+        const T* tw = reinterpret_cast<const T*>(&uw);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) hs = fmaf(to_f(out[j]), to_f(tw[j]), hs);
+      }
     } else {
       for (int j = 0; j < VEC; ++j)
         if (e0 + j < a.width) y[e0 + j] = out[j];
+      if (hw)
+        for (int j = 0; j < VEC && e0 + j < a.width; ++j) hs = fmaf(to_f(out[j]), to_f(hw[e0 + j]), hs);
+    }
+  }
+  if (hw) {
+    hs = wave_sum(hs);
+    if (lane == 0) {
+      if (a.head_z) {
+        const int m = a.head_zmap ? a.head_zmap[row] : row;
+        hs = ((unsigned)m < (unsigned)a.head_zrows) ? hs + a.head_z[m] : nan_f();
+      }
+      hs += a.head_bias;
+      if (a.head_bias_dev) hs += to_f(reinterpret_cast<const T*>(a.head_bias_dev)[0]);
+      a.head_out[row] = hs;
     }
   }
 }

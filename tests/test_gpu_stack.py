@@ -141,3 +141,28 @@ def test_full_size_stack_sampled(k, sample, fusion):
     assert np.all(np.isfinite(got["y_c"]))
     ref = oracle.oracle_forward(inp, requests=sample)
     _compare(cfg, got, ref, rows=ref["rows"], reqs=ref["requests"])
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_head_fused_into_norm_matches_standalone_head(k):
+    # The stack runs a score head that reads a norm's output inside that
+    # norm's candidate pass.  Its logits equal, bit for bit, the standalone
+    # head (rocs_head_forward) applied to the stack's own output rows.
+    from request_candidate_sharing_amd import rocs as Rr
+
+    cfg = S.small_config(k)
+    inp = S.make_inputs(cfg)
+    st, out = _stack(inp)
+    if out["logits"] is None:
+        pytest.skip("stack without a head")
+    W = np.asarray(inp["w"]["head.W"], dtype=np.float32)
+    b = float(np.asarray(inp["w"]["head.b"], dtype=np.float32).reshape(-1)[0])
+    wr, wc = st.slots[1]
+    w_cr = st.t(W[0, :wr])
+    w_cc = st.t(W[0, wr:])
+    z = torch.empty(max(st.B_r, 1), dtype=torch.float32, device="cuda")
+    lg = torch.empty(max(st.B_c, 1), dtype=torch.float32, device="cuda")
+    Rr.rocs_head_forward(st.batch, Rr.ROCS_BF16, st.y_r, wr, wr, st.y_c, wc, wc, w_cr, w_cc, b, z, lg,
+                         Rr.cur_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(lg[: st.B_c].cpu().numpy(), out["logits"])
