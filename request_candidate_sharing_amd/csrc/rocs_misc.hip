@@ -19,6 +19,20 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   if (row >= a.rows) return;
   const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
   const T* r = a.res ? reinterpret_cast<const T*>(a.res) + int64_t(row) * (a.ldres ? a.ldres : a.ldx) : nullptr;
+  // the fused head's gathered request dot, requested before the row
+  float hz = 0.f;
+  if (a.head_w && a.head_z) {
+    const int m = a.head_zmap ? a.head_zmap[row] : row;
+    hz = ((unsigned)m < (unsigned)a.head_zrows) ? a.head_z[m] : nan_f();
+  }
+  // and the head weights of this lane's chunks
+  const T* hw = reinterpret_cast<const T*>(a.head_w);
+  uint4 hwv[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e0 = (c * 64 + lane) * VEC;
+    hwv[c] = (hw && e0 + VEC <= a.width) ? *reinterpret_cast<const uint4*>(hw + e0) : make_uint4(0, 0, 0, 0);
+  }
   float v[CH][VEC];
   float s = 0.f;
 #pragma unroll
@@ -65,7 +79,6 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   }
   const T* g = reinterpret_cast<const T*>(a.gamma);
   const T* b = reinterpret_cast<const T*>(a.beta);
-  const T* hw = reinterpret_cast<const T*>(a.head_w);
   T* y = reinterpret_cast<T*>(a.y) + int64_t(row) * a.ldy;
   float hs = 0.f;  // fused head: the same chunks and order as rowdot_kernel
 #pragma unroll
@@ -85,8 +98,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
     if (e0 + VEC <= a.width) {
       *reinterpret_cast<uint4*>(y + e0) = *reinterpret_cast<const uint4*>(out);
       if (hw) {
-        const uint4 uw = *reinterpret_cast<const uint4*>(hw + e0);
-        const T* tw = reinterpret_cast<const T*>(&uw);
+        const T* tw = reinterpret_cast<const T*>(&hwv[c]);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) hs = fmaf(to_f(out[j]), to_f(tw[j]), hs);
       }
@@ -100,10 +112,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   if (hw) {
     hs = wave_sum(hs);
     if (lane == 0) {
-      if (a.head_z) {
-        const int m = a.head_zmap ? a.head_zmap[row] : row;
-        hs = ((unsigned)m < (unsigned)a.head_zrows) ? hs + a.head_z[m] : nan_f();
-      }
+      if (a.head_z) hs = hs + hz;  // NaN for a map entry out of range
       hs += a.head_bias;
       if (a.head_bias_dev) hs += to_f(reinterpret_cast<const T*>(a.head_bias_dev)[0]);
       a.head_out[row] = hs;
