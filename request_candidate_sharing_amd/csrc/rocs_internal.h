@@ -80,6 +80,8 @@ struct NormArgs {
   float* head_out;
 };
 hipError_t launch_norm(DType dt, const NormArgs& a, hipStream_t s);
+// Two independent row groups in one launch (either may be empty).
+hipError_t launch_norm2(DType dt, const NormArgs& a, const NormArgs& b, hipStream_t s);
 
 // dot rows: out[i] = w . x[i] (+ z[zmap[i]]) (+ bias)
 struct DotArgs {

@@ -1,5 +1,7 @@
 // Group-local norms, the scalar score head, the explicit broadcast used by
 // the dense-broadcast comparator, and batch validation.
+#include <algorithm>
+
 #include "rocs_device.h"
 
 namespace rocs {
@@ -11,11 +13,16 @@ namespace {
 // wave per row; the row (x + res) stays in registers between the statistics
 // and the normalisation, so each element is read once and written once.
 // LayerNorm: two-pass mean / biased variance in fp32; RMSNorm: mean square.
+// One launch can normalize two independent row groups (the request and the
+// candidate part of a stack layer): workgroups [0, nblk_a) take group pa,
+// the rest group pb.
 template <typename T, int CH>
-__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int nblk_a) {
   constexpr int VEC = 16 / sizeof(T);
+  const bool second = int(blockIdx.x) >= nblk_a;
+  const NormArgs a = second ? pb : pa;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = (second ? int(blockIdx.x) - nblk_a : int(blockIdx.x)) * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
   const T* r = a.res ? reinterpret_cast<const T*>(a.res) + int64_t(row) * (a.ldres ? a.ldres : a.ldx) : nullptr;
@@ -121,21 +128,22 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
 }
 
 template <typename T>
-hipError_t norm_dispatch(const NormArgs& a, hipStream_t s) {
+hipError_t norm_dispatch(const NormArgs& a, const NormArgs& b, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   const int per = 64 * VEC;
-  const int ch = (a.width + per - 1) / per;
-  const dim3 grid((a.rows + 3) / 4), block(256);
+  const int ch = std::max((a.width + per - 1) / per, (b.width + per - 1) / per);
+  const int na = (a.rows + 3) / 4;
+  const dim3 grid(na + (b.rows + 3) / 4), block(256);
   if (ch <= 1)
-    hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, s, a, b, na);
   else if (ch <= 2)
-    hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, s, a, b, na);
   else if (ch <= 4)
-    hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a, b, na);
   else if (ch <= 8)
-    hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a, b, na);
   else if (ch <= 16)
-    hipLaunchKernelGGL((norm_kernel<T, 16>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((norm_kernel<T, 16>), grid, block, 0, s, a, b, na);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -219,7 +227,14 @@ __global__ __launch_bounds__(256) void validate_kernel(int B_r, int B_c, const i
 
 hipError_t launch_norm(DType dt, const NormArgs& a, hipStream_t s) {
   if (a.rows <= 0 || a.width <= 0) return hipSuccess;
-  return dt == F32 ? norm_dispatch<float>(a, s) : norm_dispatch<bf16>(a, s);
+  const NormArgs none{};
+  return dt == F32 ? norm_dispatch<float>(a, none, s) : norm_dispatch<bf16>(a, none, s);
+}
+
+hipError_t launch_norm2(DType dt, const NormArgs& a, const NormArgs& b, hipStream_t s) {
+  const bool ua = a.rows > 0 && a.width > 0, ub = b.rows > 0 && b.width > 0;
+  if (!ua || !ub) return ua ? launch_norm(dt, a, s) : launch_norm(dt, b, s);
+  return dt == F32 ? norm_dispatch<float>(a, b, s) : norm_dispatch<bf16>(a, b, s);
 }
 
 hipError_t launch_rowdot(DType dt, const DotArgs& a, hipStream_t s) {
