@@ -755,7 +755,17 @@ int epilogue_variant(const GemmArgs& a) {
   }
 }
 
-bool gemm_z_in_accumulators(const GemmArgs& a) { return (epilogue_variant(a) & EPI_ZACC) != 0; }
+// bf16 launches below the candidate-size threshold that take the split-K
+// kernel (its partial sums start at zero; Z is added last).  Short chains
+// split only for request-side launches (no Z input), so candidate rows keep
+// the single-chain K order.
+bool uses_splitk(const GemmArgs& a) {
+  if (a.M >= 2048) return false;
+  const long tiles32 = long((a.M + 31) / 32) * ((a.N + 31) / 32);
+  return a.K >= 1024 || (a.z == nullptr && a.K >= 256 && tiles32 < device_cus());
+}
+
+bool gemm_z_in_accumulators(const GemmArgs& a) { return !uses_splitk(a) && (epilogue_variant(a) & EPI_ZACC) != 0; }
 
 hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   GemmArgs a = args;
@@ -786,8 +796,10 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   // 256 of them), each with seven slabs (56 KB) in flight.  Longer chains
   // split K over four waves per tile (measured, M = 128, N = 2048, K = 8960:
   // 62 -> 25 us; M = 256, N = 1024, K = 1024: 8.3 -> 5.2 us; at K = 512 the
-  // single chain is faster, 6.1 vs 7.5 us).
-  if (a.K >= 1024) return launch_tiles(gemm_bf16_splitk_kernel<4>, 32, 32, 256, a, s);
+  // single chain is faster, 6.1 vs 7.6 us), and so do short chains when there
+  // are fewer tiles than CUs (M = 32, N = 4096, K = 512: 5.8 -> 4.6 us; M =
+  // 64, N = 512, K = 256: 4.9 -> 4.1 us).
+  if (uses_splitk(a)) return launch_tiles(gemm_bf16_splitk_kernel<4>, 32, 32, 256, a, s);
   return launch_tiles(gemm_bf16_big_kernel<32, 32, 1, 1, 8>, 32, 32, 64, a, s);
 }
 
