@@ -23,8 +23,12 @@ Citations name the web pages by title:
 * [D]  "Meta推出ROCS：推荐系统推理效率提升3倍，零质量损失" (longzhangge.com
   PaperDaily digest), section on the three mechanisms.
 
-Parity status of every function is listed in ``oracle/ops.py`` and
-``oracle/stack.py`` headers.  The two stack compositions that the pages do
+* [U]  "Compute Only Once: UG-Separation for Efficient Large Recommendation
+  Models" (xllm-io review), §3 (TokenMixer layer, separation mask,
+  information compensation): ``oracle/ugsep.py``.
+
+Parity status of every function is listed in the ``oracle/ops.py``,
+``oracle/stack.py`` and ``oracle/ugsep.py`` headers.  The two stack compositions that the pages do
 not fix (the Wukong-style layer and the ranking-scale stack) are
 "parity unpinned" beyond their building blocks.
 """
@@ -42,3 +46,4 @@ from .ops import (  # noqa: F401
     decomposed_linear,
 )
 from .stack import oracle_forward, oracle_encoder  # noqa: F401
+from . import ugsep  # noqa: F401

@@ -44,6 +44,11 @@ __all__ = [
     "round_bf16",
     "glm_weight",
     "CONFIG_NAMES",
+    "UgsepConfig",
+    "ugsep_config",
+    "make_ugsep_inputs",
+    "shuffle_ugsep_candidates",
+    "UGSEP_NAMES",
 ]
 
 CONFIG_NAMES = {
@@ -307,5 +312,101 @@ def shuffle_candidates(inputs: Dict[str, Any], seed: int = 7) -> Dict[str, Any]:
     out["perm"] = perm
     out["cand2req"] = np.ascontiguousarray(inputs["cand2req"][perm])
     out["x_c"] = np.ascontiguousarray(inputs["x_c"][perm])
+    out["offsets"] = None
+    return out
+
+
+# ---------------------------------------------------------------------------
+# UG-Separation TokenMixer workload ("Compute Only Once: UG-Separation for
+# Efficient Large Recommendation Models", xllm-io review).  The token count
+# and widths follow the layer shapes of that page's W8A16 latency table
+# (16 or 8 tokens, width 1280, FFN width 2560 or 640) at its preferred
+# U:G = 1:1 split; the page gives no candidate counts, so the requests and
+# their candidate counts are the GLM MLP stack's (uniform in 64..512).
+
+UGSEP_NAMES = {
+    "tiny": "UG-Sep TokenMixer, 2 U + 2 G tokens, width 32 (parity)",
+    "small": "UG-Sep TokenMixer, 3 U + 5 G tokens, width 64 (parity)",
+    "tokenmixer": "UG-Sep TokenMixer, 8 U + 8 G tokens, width 1280, FFN 2560, 2 layers (bf16)",
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class UgsepConfig:
+    name: str
+    B: int
+    counts: tuple
+    n_u: int
+    n_g: int
+    dim: int
+    hidden: int
+    n_layers: int
+    comp: bool
+    dtype: str  # "f32" | "bf16"
+    eps: float = 1e-5
+
+    @property
+    def bf16(self) -> bool:
+        return self.dtype == "bf16"
+
+
+def ugsep_config(name: str, dtype: Optional[str] = None) -> UgsepConfig:
+    base = {
+        "tiny": UgsepConfig("tiny", 4, ("uniform", 0, 9), 2, 2, 32, 48, 2, True, "bf16"),
+        "small": UgsepConfig("small", 5, ("uniform", 0, 40), 3, 5, 64, 96, 2, True, "bf16"),
+        "tokenmixer": UgsepConfig("tokenmixer", 32, ("uniform", 64, 512), 8, 8, 1280, 2560, 2, True, "bf16"),
+    }[name]
+    return dataclasses.replace(base, dtype=dtype) if dtype else base
+
+
+def make_ugsep_inputs(cfg: UgsepConfig, seed: int = 211, counts=None) -> Dict[str, Any]:
+    """One batch and one set of layer weights for ``cfg``.
+
+    Token features ~ N(0, 1); per-token FFN weights ~ N(0, 1/fan_in) with
+    biases ~ N(0, 0.01); LayerNorm gammas ~ 1 + N(0, 0.01), betas ~ N(0,
+    0.01); compensation weights ~ N(0, 1/n_u) (or None).  Draw order: counts
+    -> x_u -> x_g -> layers in order (comp, ln1, w1, b1, w2, b2, ln2).
+    """
+    rng = np.random.default_rng(seed)
+    if counts is None:
+        spec = cfg.counts
+        if spec[0] == "uniform":
+            counts = rng.integers(spec[1], spec[2] + 1, cfg.B).astype(np.int64)
+        else:
+            counts = np.full(cfg.B, int(spec[1]), dtype=np.int64)
+    out: Dict[str, Any] = dict(make_batch(counts))
+    T, D, H = cfg.n_u + cfg.n_g, cfg.dim, cfg.hidden
+    Bc = int(out["offsets"][-1])
+    bf = cfg.bf16
+    out.update(cfg=cfg, n_u=cfg.n_u, n_g=cfg.n_g, dim=D, hidden=H, eps=cfg.eps)
+    out["x_u"] = _normal(rng, (cfg.B, cfg.n_u, D), 1.0, bf)
+    out["x_g"] = _normal(rng, (Bc, cfg.n_g, D), 1.0, bf)
+    layers = []
+    for _ in range(cfg.n_layers):
+        p: Dict[str, Any] = {}
+        p["comp"] = _normal(rng, (cfg.n_g, cfg.n_u), 1.0 / max(cfg.n_u, 1), False) if cfg.comp and cfg.n_u > 0 else None
+        g1 = _normal(rng, (D,), 0.01, False) + 1.0
+        p["ln1_g"] = round_bf16(g1) if bf else g1
+        p["ln1_b"] = _normal(rng, (D,), 0.01, bf)
+        p["w1"] = _normal(rng, (T, H, D), 1.0 / D, bf)
+        p["b1"] = _normal(rng, (T, H), 0.01, bf)
+        p["w2"] = _normal(rng, (T, D, H), 1.0 / H, bf)
+        p["b2"] = _normal(rng, (T, D), 0.01, bf)
+        g2 = _normal(rng, (D,), 0.01, False) + 1.0
+        p["ln2_g"] = round_bf16(g2) if bf else g2
+        p["ln2_b"] = _normal(rng, (D,), 0.01, bf)
+        layers.append(p)
+    out["layers"] = layers
+    return out
+
+
+def shuffle_ugsep_candidates(inputs: Dict[str, Any], seed: int = 7) -> Dict[str, Any]:
+    """Same UG-Sep batch with candidate rows in a random global order (offsets None)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(len(inputs["cand2req"]))
+    out = dict(inputs)
+    out["perm"] = perm
+    out["cand2req"] = np.ascontiguousarray(inputs["cand2req"][perm])
+    out["x_g"] = np.ascontiguousarray(inputs["x_g"][perm])
     out["offsets"] = None
     return out
