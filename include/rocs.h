@@ -45,9 +45,10 @@
  *  - cand2req values must lie in [0, B_r).  Kernels never read outside the
  *    request tensors: a candidate whose map entry is out of range gets NaN
  *    outputs.  rocs_validate_batch() checks a batch explicitly.
- *  - Results are deterministic: no atomics on any output path, and no
- *    reduction order depends on B_r, B_c or the batch composition, so a
- *    request's outputs are bit-identical whatever candidates accompany it.
+ *  - Results are deterministic: no atomics on any output path.  A launch's
+ *    reduction order depends only on its own shape (rows, width, K), so a
+ *    request's outputs are bit-identical whatever candidates accompany it,
+ *    and a candidate's whatever order the candidates come in.
  */
 #ifndef ROCS_H_
 #define ROCS_H_
@@ -318,6 +319,83 @@ typedef struct rocs_stack_io {
 size_t rocs_stack_workspace_size(const rocs_stack_desc* desc, int32_t B_r, int32_t B_c);
 int rocs_stack_forward(const rocs_stack_desc* desc, const rocs_batch* batch, const rocs_stack_io* io,
                        void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ UG-Separation TokenMixer
+ * [U] "Compute Only Once: UG-Separation for Efficient Large Recommendation
+ * Models" (xllm-io review), §3: the framework tree (U tokens, G tokens, the
+ * mask that keeps G from affecting U, U side computed once), the core
+ * formulas (TokenMixer layer P = LN(Mixup(X)), X' = LN(PFFN(P) + X), the
+ * token concatenation, the separation mask, the compensation G + Proj(U)).
+ *
+ * A sample holds T = n_u + n_g tokens of width dim, stored side by side in
+ * one row: U tokens x_u [B_r, n_u * dim] (one row per request), G tokens
+ * x_g [B_c, n_g * dim] (one row per candidate); token t starts at column
+ * t * dim.  Candidate i's sample is [U tokens of request m_i ; its G tokens].
+ * A layer computes, per sample:
+ *   G'  = G + P U            (P [n_g, n_u] fp32 token-axis map; optional)
+ *   Pm  = LN1(Mixup_UG([U ; G']))
+ *   out = LN2(PFFN(Pm) + [U ; G'])
+ * Mixup_UG: each token is cut into T chunks of width c = dim / T; output
+ * token h is the concatenation over input tokens t of chunk h of token t,
+ * except that in U outputs (h < n_u) the chunks of G tokens are zero (G may
+ * not affect U).  LN: LayerNorm over one token's dim features (biased
+ * variance), gamma/beta shared by the tokens of a layer.  PFFN: per-token
+ * weights, F_t = W2_t ReLU(W1_t Pm_t + b1_t) + b2_t.  The residual adds
+ * token h to output token h, so the U side never reads a G token: U outputs
+ * are computed once per request (B_r rows), G outputs once per candidate,
+ * reading the request's U rows and P U through cand2req.
+ *
+ * Constraints: dim a multiple of T with the chunk c a multiple of 16 bytes
+ * (8 bf16 / 4 fp32 elements), dim <= 2048 (bf16) / 1024 (fp32), hidden a
+ * multiple of 16 bytes; otherwise ROCS_ERR_SHAPE / ROCS_ERR_UNSUPPORTED /
+ * ROCS_ERR_ALIGN.  A candidate whose map entry is out of range gets NaN. */
+
+typedef struct rocs_ugsep_layer {
+  const float* comp;       /* [n_g, n_u] fp32 compensation map P; NULL = none */
+  const void* ln1_gamma;   /* [dim] */
+  const void* ln1_beta;    /* [dim] */
+  const void* w1;          /* [T, hidden, dim]: token t's first FFN weight */
+  const void* b1;          /* [T, hidden] (nullable = 0) */
+  const void* w2;          /* [T, dim, hidden] */
+  const void* b2;          /* [T, dim] (nullable = 0) */
+  const void* ln2_gamma;   /* [dim] */
+  const void* ln2_beta;    /* [dim] */
+} rocs_ugsep_layer;
+
+typedef struct rocs_ugsep_desc {
+  int32_t n_u, n_g, dim, hidden, n_layers;
+  float eps;                       /* LayerNorm epsilon, inside the root */
+  const rocs_ugsep_layer* layers;  /* host [n_layers] */
+} rocs_ugsep_desc;
+
+typedef enum rocs_ugsep_mode {
+  ROCS_UGSEP_SHARED = 0, /* U side once per request */
+  ROCS_UGSEP_DENSE = 1   /* comparator: U tokens copied to every candidate and
+                            recomputed per candidate; y_u is not written */
+} rocs_ugsep_mode;
+
+/* u_comp [B_r, n_g * dim] fp32 (ld_uc) = P x_u along the token axis (the
+ * compensation Proj(U), once per request).  No-op when B_r, n_u or n_g is 0. */
+int rocs_ugsep_compensation(rocs_dtype dtype, int32_t B_r, int32_t n_u, int32_t n_g, int32_t dim, const void* x_u,
+                            int64_t ld_xu, const float* comp, float* u_comp, int64_t ld_uc, void* stream);
+
+/* One layer's LN1(Mixup_UG(.)): p_u [B_r, n_u * dim] (U outputs of each
+ * request, ld_pu) and p_g [B_c, n_g * dim] (G outputs of each candidate,
+ * ld_pg), reading G tokens as x_g + u_comp[m_i] when u_comp is non-NULL.
+ * gamma, beta: [dim]. */
+int rocs_ugsep_mixup_norm(const rocs_batch* batch, rocs_dtype dtype, int32_t n_u, int32_t n_g, int32_t dim, float eps,
+                          const void* x_u, int64_t ld_xu, const void* x_g, int64_t ld_xg, const float* u_comp,
+                          int64_t ld_uc, const void* gamma, const void* beta, void* p_u, int64_t ld_pu, void* p_g,
+                          int64_t ld_pg, void* stream);
+
+/* n_layers TokenMixer layers: y_u [B_r, n_u * dim] (ld_yu), y_g [B_c, n_g *
+ * dim] (ld_yg).  Outputs may not alias inputs.  The workspace holds the
+ * per-token FFN activations and the inter-layer tokens. */
+size_t rocs_ugsep_workspace_size(const rocs_ugsep_desc* desc, rocs_dtype dtype, int32_t B_r, int32_t B_c,
+                                 int32_t mode);
+int rocs_ugsep_forward(const rocs_ugsep_desc* desc, const rocs_batch* batch, rocs_dtype dtype, int32_t mode,
+                       const void* x_u, int64_t ld_xu, const void* x_g, int64_t ld_xg, void* y_u, int64_t ld_yu,
+                       void* y_g, int64_t ld_yg, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ utilities */
 /* Checks offsets/cand2req on the device (synchronizes `stream`): cand2req in

@@ -852,3 +852,6 @@ int rocs_validate_batch(const rocs_batch* batch, void* stream) {
 
 // ====================================================================== stack executor
 #include "rocs_stack.inc"
+
+// ====================================================================== UG-Separation TokenMixer
+#include "rocs_ugsep.inc"

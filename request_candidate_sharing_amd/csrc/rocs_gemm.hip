@@ -545,13 +545,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_mixed_kernel(GemmArgs a, int
   }
 }
 
-// Request-side GEMMs with a long K (K >= 1024; few output tiles, each a long
-// chain of slabs): 32 x 32 output tiles, four waves per tile, wave w reducing the
+// Launches of fewer than 2,048 rows with a long K (K >= 1024; few output
+// tiles, each a long chain of slabs), and request-side launches with fewer
+// 32 x 32 tiles than CUs: 32 x 32 output tiles, four waves per tile, wave w reducing the
 // contiguous K quarter [w nk / 4, (w + 1) nk / 4) through a ring of its own
 // (no workgroup barrier in the loop).  The four fp32 partial tiles are then
 // added in a fixed order, ((p0 + p1) + p2) + p3, and wave 0 runs the
 // epilogue.  The result is deterministic; it is summed in a different order
-// than the single-chain kernels, which these request batches never use.
+// than the single-chain kernels.  The choice depends on the launch's shape
+// only (uses_splitk).
 template <int NS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a) {
   constexpr int BM = 32, BN = 32, BK = 64, CPR = 8, SLOT = (BM + BN) * CPR, SPLIT = 4;

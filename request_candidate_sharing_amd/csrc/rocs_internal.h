@@ -214,4 +214,41 @@ hipError_t launch_mlp_block(const MlpArgs& a, hipStream_t s);
 hipError_t launch_validate_batch(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, int32_t* flag,
                                  hipStream_t s);
 
+// UG-Separation TokenMixer ([U] §3).  Sample rows hold their tokens side by
+// side: x_u [rows_u, n_u * dim], x_g [rows_g, n_g * dim] (token t at column
+// t * dim).  Compensation uc [rows_u, n_g * dim] fp32 = P x_u (token axis).
+struct CompArgs {
+  int rows, n_u, n_g, dim;
+  const void* xu;
+  int64_t ldxu;
+  const float* P;  // [n_g, n_u] fp32
+  float* uc;
+  int64_t lduc;
+};
+hipError_t launch_ug_comp(DType dt, const CompArgs& a, hipStream_t s);
+
+// LayerNorm(Mixup_UG(x)) for the U outputs of rows_u requests (pu) and the
+// G outputs of rows_g candidates (pg, reading U of map[i] and G + uc[map[i]]).
+// Needs dim % (n_u + n_g) == 0, the chunk dim / (n_u + n_g) a multiple of 16
+// bytes, dim <= mixup_max_dim(dt), gamma and beta non-null.
+struct MixupArgs {
+  int rows_u, rows_g, n_u, n_g, dim;
+  const void* xu;
+  int64_t ldxu;
+  const void* xg;
+  int64_t ldxg;
+  const float* uc;  // nullable
+  int64_t lduc;
+  const int32_t* map;
+  const void* gamma;
+  const void* beta;
+  float eps;
+  void* pu;
+  int64_t ldpu;
+  void* pg;
+  int64_t ldpg;
+};
+int mixup_max_dim(DType dt);
+hipError_t launch_mixup_norm(DType dt, const MixupArgs& a, hipStream_t s);
+
 }  // namespace rocs

@@ -96,6 +96,24 @@ class rocs_stack_io(ctypes.Structure):
     ]
 
 
+class rocs_ugsep_layer(ctypes.Structure):
+    _fields_ = [
+        ("comp", c_void_p), ("ln1_gamma", c_void_p), ("ln1_beta", c_void_p), ("w1", c_void_p), ("b1", c_void_p),
+        ("w2", c_void_p), ("b2", c_void_p), ("ln2_gamma", c_void_p), ("ln2_beta", c_void_p),
+    ]
+
+
+class rocs_ugsep_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_u", c_int32), ("n_g", c_int32), ("dim", c_int32), ("hidden", c_int32), ("n_layers", c_int32),
+        ("eps", c_float), ("layers", ctypes.POINTER(rocs_ugsep_layer)),
+    ]
+
+
+ROCS_UGSEP_SHARED = 0
+ROCS_UGSEP_DENSE = 1
+
+
 class RocsError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{status_name(status)} ({status}): {msg}")
@@ -127,6 +145,11 @@ _SIGS = {
     "rocs_broadcast_rows": [P, c_int64, P, c_int64, P, c_int64, P],
     "rocs_stack_workspace_size": [P, c_int32, c_int32],
     "rocs_stack_forward": [P, P, P, P, c_size_t, P],
+    "rocs_ugsep_compensation": [c_int32, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, P, c_int64, P],
+    "rocs_ugsep_mixup_norm": [P, c_int32, c_int32, c_int32, c_int32, c_float, P, c_int64, P, c_int64, P, c_int64, P,
+                              P, P, c_int64, P, c_int64, P],
+    "rocs_ugsep_workspace_size": [P, c_int32, c_int32, c_int32, c_int32],
+    "rocs_ugsep_forward": [P, P, c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P, c_size_t, P],
     "rocs_validate_batch": [P, P],
     "rocs_status_str": [ctypes.c_int],
     "rocs_last_error": [],
@@ -136,6 +159,7 @@ _RES = {
     "rocs_dca_encode_kv_workspace_size": c_size_t,
     "rocs_dca_cross_attn_workspace_size": c_size_t,
     "rocs_stack_workspace_size": c_size_t,
+    "rocs_ugsep_workspace_size": c_size_t,
     "rocs_status_str": ctypes.c_char_p,
     "rocs_last_error": ctypes.c_char_p,
 }
@@ -287,6 +311,42 @@ def rocs_stack_workspace_size(desc: rocs_stack_desc, B_r, B_c) -> int:
 def rocs_stack_forward(desc: rocs_stack_desc, batch_, io: rocs_stack_io, workspace, ws_bytes, stream=None,
                        check=True):
     st = lib().rocs_stack_forward(ctypes.byref(desc), _b(batch_), ctypes.byref(io), ptr(workspace), ws_bytes, stream)
+    return _check(st) if check else st
+
+
+def rocs_ugsep_compensation(dtype, B_r, n_u, n_g, dim, x_u, ld_xu, comp, u_comp, ld_uc, stream=None, check=True):
+    st = lib().rocs_ugsep_compensation(dtype, B_r, n_u, n_g, dim, ptr(x_u), ld_xu, ptr(comp), ptr(u_comp), ld_uc,
+                                       stream)
+    return _check(st) if check else st
+
+
+def rocs_ugsep_mixup_norm(batch_, dtype, n_u, n_g, dim, eps, x_u, ld_xu, x_g, ld_xg, u_comp, ld_uc, gamma, beta, p_u,
+                          ld_pu, p_g, ld_pg, stream=None, check=True):
+    st = lib().rocs_ugsep_mixup_norm(_b(batch_), dtype, n_u, n_g, dim, float(eps), ptr(x_u), ld_xu, ptr(x_g), ld_xg,
+                                     ptr(u_comp), ld_uc, ptr(gamma), ptr(beta), ptr(p_u), ld_pu, ptr(p_g), ld_pg,
+                                     stream)
+    return _check(st) if check else st
+
+
+def ugsep_desc(n_u, n_g, dim, hidden, eps, layers) -> rocs_ugsep_desc:
+    """rocs_ugsep_desc over a list of per-layer dicts of device tensors (kept alive by the struct)."""
+    arr = (rocs_ugsep_layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = rocs_ugsep_layer(*(ptr(L.get(k)) for k in ("comp", "ln1_g", "ln1_b", "w1", "b1", "w2", "b2",
+                                                            "ln2_g", "ln2_b")))
+    d = rocs_ugsep_desc(n_u, n_g, dim, hidden, len(layers), float(eps), arr)
+    d._keep = (arr, layers)
+    return d
+
+
+def rocs_ugsep_workspace_size(desc: rocs_ugsep_desc, dtype, B_r, B_c, mode) -> int:
+    return int(lib().rocs_ugsep_workspace_size(ctypes.byref(desc), dtype, B_r, B_c, mode))
+
+
+def rocs_ugsep_forward(desc: rocs_ugsep_desc, batch_, dtype, mode, x_u, ld_xu, x_g, ld_xg, y_u, ld_yu, y_g, ld_yg,
+                       workspace, ws_bytes, stream=None, check=True):
+    st = lib().rocs_ugsep_forward(ctypes.byref(desc), _b(batch_), dtype, mode, ptr(x_u), ld_xu, ptr(x_g), ld_xg,
+                                  ptr(y_u), ld_yu, ptr(y_g), ld_yg, ptr(workspace), ws_bytes, stream)
     return _check(st) if check else st
 
 

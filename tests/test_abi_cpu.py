@@ -162,3 +162,57 @@ def test_binding_raises_with_message():
     with pytest.raises(R.RocsError) as e:
         R.rocs_lcb_request(R.ROCS_BF16, 4, None, 64, 64, FAKE, FAKE, None, 64, 64, 0, None, 0, FAKE, 64, FAKE, 64)
     assert "x_r" in str(e.value)
+
+
+# ---------------------------------------------------------------- UG-Separation TokenMixer (host-side checks only)
+
+def _ug_desc(n_u=8, n_g=8, dim=1280, hidden=2560, n_layers=2, comp=True, **bad):
+    layer = {k: FAKE for k in ("ln1_g", "ln1_b", "w1", "b1", "w2", "b2", "ln2_g", "ln2_b")}
+    layer["comp"] = FAKE if comp else None
+    layer.update(bad)
+    return R.ugsep_desc(n_u, n_g, dim, hidden, 1e-5, [dict(layer) for _ in range(n_layers)])
+
+
+def test_ugsep_workspace_size_is_host_logic():
+    d = _ug_desc()
+    shared = R.rocs_ugsep_workspace_size(d, R.ROCS_BF16, 32, 10056, R.ROCS_UGSEP_SHARED)
+    dense = R.rocs_ugsep_workspace_size(d, R.ROCS_BF16, 32, 10056, R.ROCS_UGSEP_DENSE)
+    # the G side's FFN activations alone: 10,056 candidates x 8 tokens x 2560 bf16
+    assert shared >= 10056 * 8 * 2560 * 2
+    assert dense > shared + 10056 * 8 * 1280 * 2  # U tokens copied to every candidate
+    assert R.rocs_ugsep_workspace_size(d, R.ROCS_F32, 32, 10056, R.ROCS_UGSEP_SHARED) > shared
+    assert R.rocs_ugsep_workspace_size(d, R.ROCS_BF16, -1, 5, 0) == 0
+    assert R.rocs_ugsep_workspace_size(d, R.ROCS_BF16, 1, 5, 7) == 0
+
+
+def test_ugsep_forward_argument_checks():
+    b = R.batch(2, 6, None, FAKE)
+
+    def fwd(desc, ws_bytes=1 << 40, dtype=R.ROCS_BF16, mode=0, ld=8 * 1280 * 2):
+        ld = ld // 2
+        return R.rocs_ugsep_forward(desc, b, dtype, mode, FAKE, ld, FAKE, ld, FAKE, ld, FAKE, ld, FAKE, ws_bytes,
+                                    check=False)
+
+    assert fwd(_ug_desc(dim=1270)) == R.ROCS_ERR_SHAPE  # not a multiple of 16 tokens
+    assert fwd(_ug_desc(n_u=4, n_g=4, dim=96)) == R.ROCS_ERR_UNSUPPORTED  # chunk of 12 bf16
+    assert fwd(_ug_desc(n_u=0, n_g=0)) == R.ROCS_ERR_INVALID_ARG
+    assert fwd(_ug_desc(hidden=2564)) == R.ROCS_ERR_ALIGN
+    assert fwd(_ug_desc(w1=None)) == R.ROCS_ERR_INVALID_ARG
+    assert fwd(_ug_desc(ln2_b=FAKE + 2)) == R.ROCS_ERR_ALIGN
+    assert fwd(_ug_desc(), mode=3) == R.ROCS_ERR_INVALID_ARG
+    assert fwd(_ug_desc(), ld=8 * 1280 * 2 - 32) == R.ROCS_ERR_SHAPE
+    need = R.rocs_ugsep_workspace_size(_ug_desc(), R.ROCS_BF16, 2, 6, 0)
+    assert fwd(_ug_desc(), ws_bytes=need - 1) == R.ROCS_ERR_WORKSPACE
+    assert "workspace" in R.last_error()
+    assert fwd(_ug_desc(dim=4096, n_u=8, n_g=8)) == R.ROCS_ERR_UNSUPPORTED  # wider than one wave's registers hold
+
+
+def test_ugsep_step_argument_checks():
+    b = R.batch(2, 6, None, FAKE)
+    st = R.rocs_ugsep_mixup_norm(b, R.ROCS_BF16, 2, 2, 64, 1e-5, FAKE, 128, FAKE, 128, None, 0, None, FAKE, FAKE,
+                                 128, FAKE, 128, check=False)
+    assert st == R.ROCS_ERR_INVALID_ARG and "gamma" in R.last_error()
+    st = R.rocs_ugsep_compensation(R.ROCS_BF16, 2, 2, 2, 64, FAKE, 128, None, FAKE, 128, check=False)
+    assert st == R.ROCS_ERR_INVALID_ARG and "comp" in R.last_error()
+    st = R.rocs_ugsep_compensation(R.ROCS_F32, 2, 2, 2, 64, FAKE, 128, FAKE, FAKE, 126, check=False)
+    assert st == R.ROCS_ERR_SHAPE
