@@ -169,15 +169,20 @@ def copy_calibration(mib=1024, reps=5):
     log(f"copy calibration: {reps} copies of {mib} MiB")
 
 
-def cpu_baseline(inp, seconds):
-    import oracle
-
+def oracle_threads() -> int:
+    """Threads of the BLAS pool the numpy oracle runs on."""
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, seconds):
+    import oracle
+
+    threads = oracle_threads()
     counts = inp["counts"]
     done, n_req, t_total = 0, 0, 0.0
     for b in range(len(counts)):
@@ -270,6 +275,60 @@ def order_study(args):
                           "shuffled_over_contiguous": res["shuffled"] / res["contiguous"]}), flush=True)
 
 
+def ugsep_work(cfg, B_r, B_c, dense=False):
+    """Algorithmic FLOPs of one UG-Sep TokenMixer step: per layer and token, the
+    two FFN GEMMs (2 * rows * dim * hidden each); the U side runs on B_r rows
+    when shared and on B_c rows in the dense comparator."""
+    R_u = B_c if dense else B_r
+    per = 2 * 2.0 * cfg.dim * cfg.hidden
+    comp = 2.0 * R_u * cfg.n_g * cfg.n_u * cfg.dim if cfg.comp else 0.0
+    return cfg.n_layers * (per * (cfg.n_u * R_u + cfg.n_g * B_c) + comp)
+
+
+def ugsep_study(args):
+    """The UG-Separation TokenMixer workload: U tokens once per request vs
+    the dense comparator that copies them to every candidate, with the CPU
+    oracle's rate on a bounded sample."""
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceUgsep
+
+    cfg = S.ugsep_config("tokenmixer")
+    inp = S.make_ugsep_inputs(cfg)
+    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+    log(f"bench: UG-Sep TokenMixer B_r={B_r} B_c={B_c}")
+    st = DeviceUgsep(inp, mode=R.ROCS_UGSEP_SHARED)
+    t_sh, _ = time_steps(st.run, args.steps, args.warmup)
+    del st
+    sh = t_sh / args.steps
+    F = ugsep_work(cfg, B_r, B_c)
+    out = {"study": "ugsep", "workload": S.UGSEP_NAMES["tokenmixer"], "B_r": B_r, "B_c": B_c,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": sh * 1e3, "candidates_per_s": B_c / sh,
+           "alg_flops_per_step": F, "mfma_util_pct": 100.0 * F / sh / PEAK_BF16}
+    if not args.no_dense:
+        de = DeviceUgsep(inp, mode=R.ROCS_UGSEP_DENSE)
+        t_de, _ = time_steps(de.run, args.steps, args.warmup)
+        del de
+        Fd = ugsep_work(cfg, B_r, B_c, dense=True)
+        out.update(dense_ms_per_step=t_de / args.steps * 1e3, speedup_vs_dense=t_de / t_sh,
+                   saved_fraction=1.0 - t_sh / t_de, flop_saved_fraction=1.0 - F / Fd,
+                   dense_mfma_util_pct=100.0 * Fd / (t_de / args.steps) / PEAK_BF16)
+    if not args.no_cpu:
+        from oracle import ugsep as U
+
+        done, t0 = 0, time.perf_counter()
+        cores = oracle_threads()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            cand = np.arange(done, min(done + 16, B_c))
+            U.ugsep_forward(inp, candidates=cand, requests=[])
+            done += len(cand)
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done / el, "unit": "candidates/s", "cores": cores, "kind": "oracle",
+                               "sample": f"oracle (fp64 numpy, per candidate) on the first {done} candidates "
+                                         f"of the same batch in {el:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +343,8 @@ def main():
                     help="profiling aid: time another workload's stack (1-5); the benchmark line is workload 2")
     ap.add_argument("--regime", action="store_true",
                     help="study: shared vs dense broadcast at N = 1..1000 candidates per request (workload 2 shapes)")
+    ap.add_argument("--ugsep", action="store_true",
+                    help="the UG-Separation TokenMixer workload (shared vs dense comparator), one JSON line")
     ap.add_argument("--order", action="store_true",
                     help="study: contiguous vs shuffled candidate order on workloads 2-5")
     ap.add_argument("--shuffle", action="store_true",
@@ -311,6 +372,8 @@ def main():
         return regime_study(args)
     if args.order:
         return order_study(args)
+    if args.ugsep:
+        return ugsep_study(args)
     if args.workload != 2:
         return other_workload(args)
     cfg = S.config(2)

@@ -555,7 +555,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_mixed_kernel(GemmArgs a, int
 // than the single-chain kernels.  The choice depends on the launch's shape
 // only (uses_splitk).
 template <int NS>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a0) {
+  const GemmArgs a = batch_slice(a0, blockIdx.y);  // GEMM blockIdx.y of a batch
   constexpr int BM = 32, BN = 32, BK = 64, CPR = 8, SLOT = (BM + BN) * CPR, SPLIT = 4;
   __shared__ uint4 smem[SPLIT * NS * SLOT];
   using Feed = SlabFeed<BM, BN, 1>;
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 template <typename K>
 hipError_t launch_tiles(K kernel, int bm, int bn, int threads, const GemmArgs& a, hipStream_t s) {
   const int nwg = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
-  hipLaunchKernelGGL(kernel, dim3(nwg), dim3(threads), 0, s, a);
+  hipLaunchKernelGGL(kernel, dim3(nwg, a.batch > 1 ? a.batch : 1), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -773,6 +774,18 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   GemmArgs a = args;
   a.epi = epilogue_variant(a);
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  // A batch runs as one launch (grid.y = GEMM) on the split-K kernel, whose
+  // few tiles per GEMM leave most of the chip idle; any other kernel choice
+  // runs the GEMMs one launch each.
+  if (a.batch > 1 && !(dt == BF16 && uses_splitk(a))) {
+    for (int i = 0; i < a.batch; ++i) {
+      GemmArgs b = batch_slice(args, i);
+      b.batch = 1;
+      const hipError_t e = launch_gemm(dt, b, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (dt == F32) return launch_tiles(gemm_f32_kernel, 64, 64, 256, a, s);
   // All bf16 variants compute every element identically; the choice only
   // trades tile size against the number of workgroups.  Measured on the

@@ -46,7 +46,26 @@ struct GemmArgs {
   const void* res;
   int64_t ldres;
   int epi;  // epilogue variant, set by launch_gemm (callers leave it 0)
+  // Optional batch of `batch` independent GEMMs of this shape: GEMM i reads
+  // A, W[*], bias, res and writes out0 at i times these byte strides (Z,
+  // out1 and zmap are shared).  0 or 1 = one GEMM.
+  int batch;
+  int64_t sA, sW, s0, sbias, sres;
 };
+
+// GEMM i of a batched launch (pointers advanced by i strides).
+__host__ __device__ inline GemmArgs batch_slice(const GemmArgs& a, int i) {
+  GemmArgs b = a;
+  if (i > 0) {
+    b.A = static_cast<const char*>(a.A) + i * a.sA;
+    for (int k = 0; k < 4; ++k)
+      if (a.W[k]) b.W[k] = static_cast<const char*>(a.W[k]) + i * a.sW;
+    b.out0 = static_cast<char*>(a.out0) + i * a.s0;
+    if (a.bias) b.bias = static_cast<const char*>(a.bias) + i * a.sbias;
+    if (a.res) b.res = static_cast<const char*>(a.res) + i * a.sres;
+  }
+  return b;
+}
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
 // Whether launch_gemm sums this launch as Z + products (accumulators started

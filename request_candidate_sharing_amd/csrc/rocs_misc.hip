@@ -16,7 +16,8 @@ namespace {
 // One launch can normalize two independent row groups (the request and the
 // candidate part of a stack layer): workgroups [0, nblk_a) take group pa,
 // the rest group pb.
-template <typename T, int CH>
+// RES: some group of the launch adds a residual (the other may not).
+template <typename T, int CH, bool RES>
 __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int nblk_a) {
   constexpr int VEC = 16 / sizeof(T);
   const bool second = int(blockIdx.x) >= nblk_a;
@@ -40,6 +41,35 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
     const int e0 = (c * 64 + lane) * VEC;
     hwv[c] = (hw && e0 + VEC <= a.width) ? *reinterpret_cast<const uint4*>(hw + e0) : make_uint4(0, 0, 0, 0);
   }
+  // every chunk's loads are issued before any is used, so a wave keeps all
+  // of its row's 16-byte loads in flight at once
+  // (one uniform branch around all of them: a lane whose vector is not
+  // whole in the row loads the row's last whole vector instead and ignores
+  // it; rows narrower than one vector take the element path below)
+  // with RES the residual is loaded unconditionally (from x when this group
+  // has none) and added by a select, so no branch separates the loads
+  const bool has_r = RES && a.res != nullptr;
+  const T* rp = (RES && r) ? r : x;
+  uint4 xq[CH], rq[CH];
+  const int last_vec = (a.width / VEC - 1) * VEC;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) xq[c] = rq[c] = make_uint4(0, 0, 0, 0);
+  if (a.width >= VEC) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e0 = (c * 64 + lane) * VEC;
+      const int el = e0 + VEC <= a.width ? e0 : last_vec;
+      xq[c] = *reinterpret_cast<const uint4*>(x + el);
+      if (RES) rq[c] = *reinterpret_cast<const uint4*>(rp + el);
+    }
+  }
+  // Each loaded value is consumed here, in chunk order, after the last load
+  // was issued: the compiler may not move a load down next to its use.
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    asm volatile("" ::"v"(xq[c].x), "v"(xq[c].y), "v"(xq[c].z), "v"(xq[c].w) : "memory");
+    if (RES) asm volatile("" ::"v"(rq[c].x), "v"(rq[c].y), "v"(rq[c].z), "v"(rq[c].w) : "memory");
+  }
   float v[CH][VEC];
   float s = 0.f;
 #pragma unroll
@@ -48,15 +78,13 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
 #pragma unroll
     for (int j = 0; j < VEC; ++j) v[c][j] = 0.f;
     if (e0 + VEC <= a.width) {
-      const uint4 u = *reinterpret_cast<const uint4*>(x + e0);
-      const T* t = reinterpret_cast<const T*>(&u);
+      const T* t = reinterpret_cast<const T*>(&xq[c]);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) v[c][j] = to_f(t[j]);
-      if (r) {
-        const uint4 ur = *reinterpret_cast<const uint4*>(r + e0);
-        const T* tr = reinterpret_cast<const T*>(&ur);
+      if (RES) {
+        const T* tr = reinterpret_cast<const T*>(&rq[c]);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) v[c][j] += to_f(tr[j]);
+        for (int j = 0; j < VEC; ++j) v[c][j] = has_r ? v[c][j] + to_f(tr[j]) : v[c][j];
       }
     } else {
       for (int j = 0; j < VEC; ++j)
@@ -92,13 +120,26 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
   for (int c = 0; c < CH; ++c) {
     const int e0 = (c * 64 + lane) * VEC;
     if (e0 >= a.width) continue;
+    // affine parameters of this chunk in 16-byte loads (gamma and beta are
+    // 16-byte aligned); the ragged last chunk reads them element by element
+    T gv[VEC], bv[VEC];
+    if (e0 + VEC <= a.width) {
+      if (g) *reinterpret_cast<uint4*>(gv) = *reinterpret_cast<const uint4*>(g + e0);
+      if (b) *reinterpret_cast<uint4*>(bv) = *reinterpret_cast<const uint4*>(b + e0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const int e = min(e0 + j, a.width - 1);
+        if (g) gv[j] = g[e];
+        if (b) bv[j] = b[e];
+      }
+    }
     T out[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-      const int e = min(e0 + j, a.width - 1);
       float t = (v[c][j] - mean) * scale;
-      if (g) t *= to_f(g[e]);
-      if (b) t += to_f(b[e]);
+      if (g) t *= to_f(gv[j]);
+      if (b) t += to_f(bv[j]);
       if (a.act == 1) t = fmaxf(t, 0.f);
       out[j] = from_f<T>(t);
     }
@@ -127,26 +168,30 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
   }
 }
 
+template <typename T, bool RES>
+hipError_t norm_launch(int ch, dim3 grid, const NormArgs& a, const NormArgs& b, int na, hipStream_t s) {
+  const dim3 block(256);
+  switch (ch <= 1 ? 1 : ch <= 2 ? 2 : ch <= 3 ? 3 : ch <= 4 ? 4 : ch <= 8 ? 8 : ch <= 16 ? 16 : 0) {
+    case 1: hipLaunchKernelGGL((norm_kernel<T, 1, RES>), grid, block, 0, s, a, b, na); break;
+    case 2: hipLaunchKernelGGL((norm_kernel<T, 2, RES>), grid, block, 0, s, a, b, na); break;
+    case 3: hipLaunchKernelGGL((norm_kernel<T, 3, RES>), grid, block, 0, s, a, b, na); break;
+    case 4: hipLaunchKernelGGL((norm_kernel<T, 4, RES>), grid, block, 0, s, a, b, na); break;
+    case 8: hipLaunchKernelGGL((norm_kernel<T, 8, RES>), grid, block, 0, s, a, b, na); break;
+    case 16: hipLaunchKernelGGL((norm_kernel<T, 16, RES>), grid, block, 0, s, a, b, na); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t norm_dispatch(const NormArgs& a, const NormArgs& b, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   const int per = 64 * VEC;
   const int ch = std::max((a.width + per - 1) / per, (b.width + per - 1) / per);
   const int na = (a.rows + 3) / 4;
-  const dim3 grid(na + (b.rows + 3) / 4), block(256);
-  if (ch <= 1)
-    hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, s, a, b, na);
-  else if (ch <= 2)
-    hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, s, a, b, na);
-  else if (ch <= 4)
-    hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a, b, na);
-  else if (ch <= 8)
-    hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a, b, na);
-  else if (ch <= 16)
-    hipLaunchKernelGGL((norm_kernel<T, 16>), grid, block, 0, s, a, b, na);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 grid(na + (b.rows + 3) / 4);
+  if (grid.x == 0) return hipSuccess;
+  return (a.res || b.res) ? norm_launch<T, true>(ch, grid, a, b, na, s) : norm_launch<T, false>(ch, grid, a, b, na, s);
 }
 
 // ----------------------------------------------------------------- row dot (score head)

@@ -61,37 +61,51 @@ __global__ __launch_bounds__(256) void mixup_norm_kernel(MixupArgs a, int nblk_u
   const T* xu = reinterpret_cast<const T*>(a.xu) + int64_t(bad ? 0 : b) * a.ldxu;
   const T* xg = gside ? reinterpret_cast<const T*>(a.xg) + int64_t(s) * a.ldxg : nullptr;
   const float* uc = (gside && a.uc) ? a.uc + int64_t(bad ? 0 : b) * a.lduc : nullptr;
+  // all loads of the row first (kept in flight together), then the sums
+  // Branch-free: every lane loads from an address inside its sample's rows
+  // (lanes past the row end, and U-output lanes on G chunks, load a valid U
+  // vector instead) and keeps or drops the value by a select afterwards.
+  // Chunks that start past the row are skipped by a uniform test.
+  uint4 raw[CH];
+  float4 cq[CH][VEC / 4];
+  bool keep[CH], comp[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e0 = (c * 64 + lane) * VEC;
+    raw[c] = make_uint4(0, 0, 0, 0);
+    keep[c] = comp[c] = false;
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) cq[c][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c * 64 * VEC < a.dim) {
+      const int ec = min(e0, a.dim - VEC);
+      const int t = ec / cw;
+      const int col = h * cw + (ec - t * cw);
+      const bool from_u = t < a.n_u, from_g = !from_u && gside;
+      keep[c] = e0 < a.dim && (from_u || from_g);
+      const int tg = max(t - a.n_u, 0);
+      const T* src = from_g ? xg + tg * a.dim + col : xu + int64_t(from_u ? t : 0) * a.dim + col;
+      raw[c] = *reinterpret_cast<const uint4*>(src);
+      if (uc) {
+        comp[c] = keep[c] && from_g;
+#pragma unroll
+        for (int k = 0; k < VEC / 4; ++k) cq[c][k] = *reinterpret_cast<const float4*>(uc + tg * a.dim + col + 4 * k);
+      }
+    }
+  }
   float v[CH][VEC];
   float sum = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int e0 = (c * 64 + lane) * VEC;
+    const T* tw = reinterpret_cast<const T*>(&raw[c]);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) v[c][j] = 0.f;
-    if (e0 < a.dim) {
-      const int t = e0 / cw;
-      const int col = h * cw + (e0 - t * cw);
-      if (t < a.n_u) {
-        const uint4 w = *reinterpret_cast<const uint4*>(xu + int64_t(t) * a.dim + col);
-        const T* tw = reinterpret_cast<const T*>(&w);
+    for (int j = 0; j < VEC; ++j) v[c][j] = keep[c] ? to_f(tw[j]) : 0.f;
+    if (comp[c]) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) v[c][j] = to_f(tw[j]);
-      } else if (gside) {
-        const int off = (t - a.n_u) * a.dim + col;
-        const uint4 w = *reinterpret_cast<const uint4*>(xg + off);
-        const T* tw = reinterpret_cast<const T*>(&w);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) v[c][j] = to_f(tw[j]);
-        if (uc) {
-#pragma unroll
-          for (int j = 0; j < VEC; j += 4) {
-            const float4 f = *reinterpret_cast<const float4*>(uc + off + j);
-            v[c][j] += f.x;
-            v[c][j + 1] += f.y;
-            v[c][j + 2] += f.z;
-            v[c][j + 3] += f.w;
-          }
-        }
+      for (int k = 0; k < VEC / 4; ++k) {
+        v[c][4 * k] += cq[c][k].x;
+        v[c][4 * k + 1] += cq[c][k].y;
+        v[c][4 * k + 2] += cq[c][k].z;
+        v[c][4 * k + 3] += cq[c][k].w;
       }
     }
 #pragma unroll

@@ -231,3 +231,45 @@ class DeviceStack:
         out = {"y_r": self.y_r.float().cpu().numpy(), "y_c": self.y_c[: self.B_c].float().cpu().numpy()}
         out["logits"] = self.logits[: self.B_c].cpu().numpy() if self.has_head else None
         return out
+
+
+class DeviceUgsep:
+    """The UG-Separation TokenMixer workload ("Compute Only Once:
+    UG-Separation for Efficient Large Recommendation Models", xllm-io review,
+    §3) on a GPU: token rows, per-layer weights, descriptor, workspace and
+    outputs.  Marshalling only; rocs_ugsep_forward does the work."""
+
+    def __init__(self, inputs: Dict[str, Any], device="cuda", mode: int = R.ROCS_UGSEP_SHARED):
+        torch = _torch()
+        self.inputs, self.mode = inputs, mode
+        cfg = inputs["cfg"]
+        self.dtype = R.ROCS_BF16 if cfg.dtype == "bf16" else R.ROCS_F32
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        n_u, n_g, D, H = inputs["n_u"], inputs["n_g"], inputs["dim"], inputs["hidden"]
+        self.B_r, self.B_c = inputs["x_u"].shape[0], inputs["x_g"].shape[0]
+
+        def t(a, dt=tdt):
+            return torch.as_tensor(np.ascontiguousarray(a, dtype=np.float32), device=device).to(dt).contiguous()
+
+        self.x_u = t(np.asarray(inputs["x_u"]).reshape(self.B_r, n_u * D))
+        self.x_g = t(np.asarray(inputs["x_g"]).reshape(self.B_c, n_g * D))
+        self.y_u = torch.empty(max(self.B_r, 1), max(n_u * D, 8), dtype=tdt, device=device)
+        self.y_g = torch.empty(max(self.B_c, 1), max(n_g * D, 8), dtype=tdt, device=device)
+        self.c2r = torch.as_tensor(inputs["cand2req"], dtype=torch.int32, device=device)
+        offs = inputs.get("offsets")
+        self.offs = None if offs is None else torch.as_tensor(offs, dtype=torch.int32, device=device)
+        layers = []
+        for p in inputs["layers"]:
+            d = {k: t(p[k]) for k in ("ln1_g", "ln1_b", "w1", "b1", "w2", "b2", "ln2_g", "ln2_b")}
+            d["comp"] = None if p["comp"] is None else t(p["comp"], torch.float32)
+            layers.append(d)
+        self.desc = R.ugsep_desc(n_u, n_g, D, H, inputs["eps"], layers)
+        self.batch = R.batch(self.B_r, self.B_c, self.offs, self.c2r)
+        self.ws_bytes = R.rocs_ugsep_workspace_size(self.desc, self.dtype, self.B_r, self.B_c, mode)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ld_u, self.ld_g = max(n_u * D, 8), max(n_g * D, 8)
+
+    def run(self, stream: Optional[int] = None):
+        R.rocs_ugsep_forward(self.desc, self.batch, self.dtype, self.mode, self.x_u, self.ld_u, self.x_g, self.ld_g,
+                             self.y_u, self.ld_u, self.y_g, self.ld_g, self.ws, self.ws_bytes,
+                             R.cur_stream() if stream is None else stream)
