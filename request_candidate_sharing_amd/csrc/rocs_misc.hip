@@ -64,11 +64,14 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
     }
   }
   // Each loaded value is consumed here, in chunk order, after the last load
-  // was issued: the compiler may not move a load down next to its use.
+  // was issued: the compiler may not move a load down next to its use (with
+  // one chunk there is nothing to order).
+  if constexpr (CH > 1) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    asm volatile("" ::"v"(xq[c].x), "v"(xq[c].y), "v"(xq[c].z), "v"(xq[c].w) : "memory");
-    if (RES) asm volatile("" ::"v"(rq[c].x), "v"(rq[c].y), "v"(rq[c].z), "v"(rq[c].w) : "memory");
+    for (int c = 0; c < CH; ++c) {
+      asm volatile("" ::"v"(xq[c].x), "v"(xq[c].y), "v"(xq[c].z), "v"(xq[c].w) : "memory");
+      if (RES) asm volatile("" ::"v"(rq[c].x), "v"(rq[c].y), "v"(rq[c].z), "v"(rq[c].w) : "memory");
+    }
   }
   float v[CH][VEC];
   float s = 0.f;
