@@ -25,7 +25,8 @@ Citations name the web pages by title:
 
 * [U]  "Compute Only Once: UG-Separation for Efficient Large Recommendation
   Models" (xllm-io review), §3 (TokenMixer layer, separation mask,
-  information compensation): ``oracle/ugsep.py``.
+  information compensation): ``oracle/ugsep.py``; stage 4 and the W8A16
+  configuration (8-bit float weights, bf16 activations): ``oracle/w8a16.py``.
 
 Parity status of every function is listed in the ``oracle/ops.py``,
 ``oracle/stack.py`` and ``oracle/ugsep.py`` headers.  The two stack compositions that the pages do
@@ -46,4 +47,4 @@ from .ops import (  # noqa: F401
     decomposed_linear,
 )
 from .stack import oracle_forward, oracle_encoder  # noqa: F401
-from . import ugsep  # noqa: F401
+from . import ugsep, w8a16  # noqa: F401

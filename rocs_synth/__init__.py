@@ -410,3 +410,26 @@ def shuffle_ugsep_candidates(inputs: Dict[str, Any], seed: int = 7) -> Dict[str,
     out["x_g"] = np.ascontiguousarray(inputs["x_g"][perm])
     out["offsets"] = None
     return out
+
+
+# ---------------------------------------------------------------------------
+# W8A16 linear layer (8-bit float weights, bf16 activations; "Compute Only
+# Once: UG-Separation ...", W8A16 configuration).  The page's latency table
+# lists layer shapes (batch 1; 16 or 8 tokens; width 1280; 2560 or 640
+# outputs).
+
+W8A16_SHAPES = [(16, 1280, 2560), (16, 1280, 640), (8, 1280, 2560), (8, 1280, 640)]  # (M tokens, K, N)
+
+
+def make_w8a16_inputs(M: int, K: int, N: int, seed: int = 5, bias: bool = True) -> Dict[str, Any]:
+    """x ~ N(0, 1) (bf16 values); weight codes drawn uniformly from the
+    finite 8-bit E4M3 codes (every byte except the two NaN codes 0x7F and
+    0xFF); per-output-channel scales ~ U(0.5, 1.5) / (16 sqrt(K)); bias ~
+    N(0, 0.01) (bf16 values).  Draw order: x, codes, scales, bias."""
+    rng = np.random.default_rng(seed)
+    x = round_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    codes = rng.integers(0, 254, (N, K)).astype(np.uint8)
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)  # skip 0x7F; 0xFF is never drawn
+    scale = (rng.uniform(0.5, 1.5, N) / (16.0 * math.sqrt(K))).astype(np.float32)
+    b = round_bf16((rng.standard_normal(N) * 0.1).astype(np.float32)) if bias else None
+    return {"x": x, "codes": codes, "scale": scale, "bias": b}
