@@ -397,6 +397,24 @@ int rocs_ugsep_forward(const rocs_ugsep_desc* desc, const rocs_batch* batch, roc
                        const void* x_u, int64_t ld_xu, const void* x_g, int64_t ld_xg, void* y_u, int64_t ld_yu,
                        void* y_g, int64_t ld_yg, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ W8A16 linear
+ * [U] "Compute Only Once: UG-Separation for Efficient Large Recommendation
+ * Models" (xllm-io review), §3 framework tree stage 4 and the W8A16
+ * configuration table: weights stored in 8 bits, activations in bf16, for
+ * the memory-bound small-batch layers.
+ *   y[m, n] = act( sum_k x[m, k] * w_scale[n] * e4m3(w_q[n, k]) + bias[n] )
+ * w_q: [N, K] bytes (ld_w bytes per row), each the 8-bit E4M3 encoding with
+ * no infinities (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent 0 is subnormal; S.1111.111 is NaN; largest magnitude 448).
+ * w_scale: [N] fp32, one scale per output channel.  x: [M, K] bf16 (ld_x),
+ * bias: [N] bf16 (nullable), y: [M, N] bf16 (ld_y).  Products accumulate in
+ * fp32; the scale, bias and ReLU are applied once at the end.
+ * Supported: 1 <= M <= 64, N a multiple of 32, K a positive multiple of 128
+ * (ROCS_ERR_UNSUPPORTED otherwise); x, w_q, y 16-byte aligned with 16-byte
+ * row strides (ROCS_ERR_ALIGN).  M == 0 or N == 0 is a no-op. */
+int rocs_w8a16_linear(int32_t M, int32_t N, int32_t K, const void* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,
+                      const float* w_scale, const void* bias, rocs_act act, void* y, int64_t ld_y, void* stream);
+
 /* ------------------------------------------------------------------ utilities */
 /* Checks offsets/cand2req on the device (synchronizes `stream`): cand2req in
  * range, and when offsets is given, offsets[0] == 0, offsets[B_r] == B_c,

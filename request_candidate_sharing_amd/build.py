@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librocs.so")
 
-SOURCES = ["rocs_gemm.hip", "rocs_mlp.hip", "rocs_misc.hip", "rocs_attn.hip", "rocs_fm.hip", "rocs_ugsep.hip", "rocs_api.cpp"]
+SOURCES = ["rocs_gemm.hip", "rocs_mlp.hip", "rocs_misc.hip", "rocs_attn.hip", "rocs_fm.hip", "rocs_ugsep.hip", "rocs_w8a16.hip", "rocs_api.cpp"]
 
 # Packed fp32 VALU forms are disabled for every translation unit.
 HIP_FLAGS = [

@@ -855,3 +855,6 @@ int rocs_validate_batch(const rocs_batch* batch, void* stream) {
 
 // ====================================================================== UG-Separation TokenMixer
 #include "rocs_ugsep.inc"
+
+// ====================================================================== W8A16 linear
+#include "rocs_w8a16.inc"

@@ -268,6 +268,23 @@ struct MixupArgs {
   int64_t ldpg;
 };
 int mixup_max_dim(DType dt);
+
+// W8A16 linear: y = act(x (scale . fp8(wq))^T + bias); x [M, K] bf16 (ldx),
+// wq [N, K] E4M3 codes (ldw bytes), scale [N] fp32, bias [N] bf16 or null,
+// y [M, N] bf16 (ldy).  Needs 1 <= M <= 64, N % 32 == 0, K % 128 == 0.
+struct W8Args {
+  int M, N, K;
+  const bf16* x;
+  int64_t ldx;
+  const uint8_t* wq;
+  int64_t ldw;
+  const float* scale;
+  const bf16* bias;
+  int act;
+  bf16* y;
+  int64_t ldy;
+};
+hipError_t launch_w8a16(const W8Args& a, hipStream_t s);
 hipError_t launch_mixup_norm(DType dt, const MixupArgs& a, hipStream_t s);
 
 }  // namespace rocs

@@ -150,6 +150,7 @@ _SIGS = {
                               P, P, c_int64, P, c_int64, P],
     "rocs_ugsep_workspace_size": [P, c_int32, c_int32, c_int32, c_int32],
     "rocs_ugsep_forward": [P, P, c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P, c_size_t, P],
+    "rocs_w8a16_linear": [c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, c_int32, P, c_int64, P],
     "rocs_validate_batch": [P, P],
     "rocs_status_str": [ctypes.c_int],
     "rocs_last_error": [],
@@ -347,6 +348,12 @@ def rocs_ugsep_forward(desc: rocs_ugsep_desc, batch_, dtype, mode, x_u, ld_xu, x
                        workspace, ws_bytes, stream=None, check=True):
     st = lib().rocs_ugsep_forward(ctypes.byref(desc), _b(batch_), dtype, mode, ptr(x_u), ld_xu, ptr(x_g), ld_xg,
                                   ptr(y_u), ld_yu, ptr(y_g), ld_yg, ptr(workspace), ws_bytes, stream)
+    return _check(st) if check else st
+
+
+def rocs_w8a16_linear(M, N, K, x, ld_x, w_q, ld_w, w_scale, bias, act, y, ld_y, stream=None, check=True):
+    st = lib().rocs_w8a16_linear(M, N, K, ptr(x), ld_x, ptr(w_q), ld_w, ptr(w_scale), ptr(bias), act, ptr(y), ld_y,
+                                 stream)
     return _check(st) if check else st
 
 

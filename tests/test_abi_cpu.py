@@ -216,3 +216,18 @@ def test_ugsep_step_argument_checks():
     assert st == R.ROCS_ERR_INVALID_ARG and "comp" in R.last_error()
     st = R.rocs_ugsep_compensation(R.ROCS_F32, 2, 2, 2, 64, FAKE, 128, FAKE, FAKE, 126, check=False)
     assert st == R.ROCS_ERR_SHAPE
+
+
+def test_w8a16_argument_checks():
+    def call(M=16, N=2560, K=1280, x=FAKE, ldx=1280, w=FAKE, ldw=1280, s=FAKE, y=FAKE, ldy=2560, act=0):
+        return R.rocs_w8a16_linear(M, N, K, x, ldx, w, ldw, s, None, act, y, ldy, check=False)
+
+    assert call(M=65) == R.ROCS_ERR_UNSUPPORTED
+    assert call(N=2550) == R.ROCS_ERR_UNSUPPORTED
+    assert call(K=1200, ldx=1200, ldw=1200) == R.ROCS_ERR_UNSUPPORTED
+    assert call(x=FAKE + 2) == R.ROCS_ERR_ALIGN
+    assert call(ldw=1272) == R.ROCS_ERR_SHAPE
+    assert call(ldw=1288 + 4) == R.ROCS_ERR_ALIGN  # byte stride not a multiple of 16
+    assert call(s=None) == R.ROCS_ERR_INVALID_ARG and "w_scale" in R.last_error()
+    assert call(act=5) == R.ROCS_ERR_INVALID_ARG
+    assert call(M=0) == R.ROCS_OK  # empty: nothing launched

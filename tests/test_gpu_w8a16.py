@@ -1,0 +1,90 @@
+"""GPU parity of the W8A16 linear layer against the CPU oracle.
+
+Citation: "Compute Only Once: UG-Separation for Efficient Large
+Recommendation Models" (xllm-io review), §3 stage 4 and the W8A16
+configuration.  Calls go through the C ABI.  The decode of every finite
+E4M3 code is checked bit for bit (one-hot activation rows pick single
+weights; every E4M3 value is exact in bf16); the layer itself within the
+bf16 bound (2e-2 of the largest output), at the page's four latency-table
+shapes and at ragged ones, with padded leading dimensions.
+"""
+
+import numpy as np
+import pytest
+
+import rocs_synth as S
+from oracle import w8a16 as W
+from gpu_util import TOL_BF16, rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _R():
+    from request_candidate_sharing_amd import rocs as R
+
+    return R
+
+
+def run(x, codes, scale, bias, act, pad=0):
+    R = _R()
+    M, K = x.shape
+    N = codes.shape[0]
+    ldx, ldw, ldy = K + pad, K + 16 * (pad > 0), N + pad
+    xs = torch.full((M, ldx), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xs[:, :K] = torch.as_tensor(x, device="cuda").to(torch.bfloat16)
+    ws = torch.zeros((N, ldw), dtype=torch.uint8, device="cuda")
+    ws[:, :K] = torch.as_tensor(codes, device="cuda")
+    ys = torch.full((M, ldy), float("nan"), dtype=torch.bfloat16, device="cuda")
+    b = None if bias is None else torch.as_tensor(bias, device="cuda").to(torch.bfloat16)
+    R.rocs_w8a16_linear(M, N, K, xs, ldx, ws, ldw, torch.as_tensor(scale, dtype=torch.float32, device="cuda"), b,
+                        act, ys, ldy, R.cur_stream())
+    torch.cuda.synchronize()
+    if pad:
+        assert torch.isnan(ys[:, N:]).all()
+    return ys[:, :N].float().cpu().numpy()
+
+
+def test_every_finite_code_decodes_exactly():
+    M, N, K = 32, 256, 128
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(M), np.arange(M)] = 1.0  # row m picks weight column m
+    codes = np.zeros((N, K), np.uint8)
+    for k in range(M):
+        c = (np.arange(N) + 8 * k) % 256
+        codes[:, k] = np.where((c & 0x7F) == 0x7F, 0, c)
+    y = run(x, codes, np.ones(N, np.float32), None, 0)
+    ref = W.decode_e4m3(codes[:, :M]).T  # [m, n]
+    np.testing.assert_array_equal(y, ref)
+    seen = set(codes[:, :M].ravel().tolist())
+    assert len(seen) == 254  # every code but the two NaN codes
+
+
+def test_nan_code_poisons_its_output_channel_only():
+    d = S.make_w8a16_inputs(4, 128, 64, seed=9)
+    codes = d["codes"].copy()
+    codes[5, 17] = 0x7F
+    y = run(d["x"], codes, d["scale"], d["bias"], 0)
+    assert np.isnan(y[:, 5]).all()
+    assert np.isfinite(np.delete(y, 5, axis=1)).all()
+
+
+CASES = [  # M, K, N, bias, act, padded
+    (16, 1280, 2560, True, 0, 0),
+    (16, 1280, 640, True, 1, 0),
+    (8, 1280, 2560, False, 0, 0),
+    (8, 1280, 640, True, 0, 0),
+    (1, 128, 64, True, 1, 8),
+    (37, 384, 96, True, 0, 8),
+    (64, 256, 32, False, 1, 0),
+    (33, 1024, 128, True, 1, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bias,act,pad", CASES)
+def test_linear_matches_oracle(M, K, N, bias, act, pad):
+    d = S.make_w8a16_inputs(M, K, N, seed=M + K + N, bias=bias)
+    y = run(d["x"], d["codes"], d["scale"], d["bias"], act, pad)
+    ref = W.w8a16_linear(d["x"], d["codes"], d["scale"], d["bias"], act)
+    assert rel_err(y, ref) <= TOL_BF16
