@@ -329,6 +329,56 @@ def ugsep_study(args):
     print(json.dumps(out), flush=True)
 
 
+def w8a16_study(args):
+    """Latency of the W8A16 linear layer against the bf16 GEMM of the same
+    shape, at the layer shapes of the UG-Separation page's W8A16 table.
+    Weights rotate over buffer sets larger than the 256 MB MALL, so each
+    launch streams its weights from HBM as a layer of a deep model would."""
+    import torch
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+
+    page = {(16, 1280, 2560): -50.2, (16, 1280, 640): -40.0, (8, 1280, 2560): -46.8, (8, 1280, 640): -55.0}
+    st = R.cur_stream()
+    # the page's shapes, then two larger ones where the weight stream dominates
+    for (M, K, N) in S.W8A16_SHAPES + [(16, 4096, 4096), (16, 8192, 8192)]:
+        d = S.make_w8a16_inputs(M, K, N)
+        x = torch.as_tensor(d["x"], device="cuda").to(torch.bfloat16)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        b = torch.as_tensor(d["bias"], device="cuda").to(torch.bfloat16)
+        sc = torch.as_tensor(d["scale"], device="cuda")
+        sets8 = max(2, (320 << 20) // (N * K))
+        sets16 = max(2, (320 << 20) // (2 * N * K))
+        wq = torch.as_tensor(d["codes"], device="cuda").unsqueeze(0).repeat(sets8, 1, 1)
+        wb = torch.randn(sets16, N, K, device="cuda").to(torch.bfloat16)
+
+        def t8(i):
+            R.rocs_w8a16_linear(M, N, K, x, K, wq[i % sets8], K, sc, b, 0, y, N, st)
+
+        def t16(i):
+            R.rocs_lcb_request(R.ROCS_BF16, M, x, K, K, wb[i % sets16], None, b, N, 0, 0, None, 0, y, N, None, 0, st)
+
+        res = {}
+        for name, fn in (("w8a16", t8), ("bf16", t16)):
+            for i in range(args.warmup * 10):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(args.steps * 20, 200)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"study": "w8a16", "M": M, "K": K, "N": N, "w8a16_us": res["w8a16"], "bf16_us": res["bf16"],
+                          "latency_change_pct": 100.0 * (res["w8a16"] / res["bf16"] - 1.0),
+                          "page_latency_change_pct": page.get((M, K, N)),
+                          "w8a16_weight_GBps": N * K / res["w8a16"] / 1e3,
+                          "bf16_weight_GBps": 2 * N * K / res["bf16"] / 1e3}), flush=True)
+        del wq, wb
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +395,8 @@ def main():
                     help="study: shared vs dense broadcast at N = 1..1000 candidates per request (workload 2 shapes)")
     ap.add_argument("--ugsep", action="store_true",
                     help="the UG-Separation TokenMixer workload (shared vs dense comparator), one JSON line")
+    ap.add_argument("--w8a16", action="store_true",
+                    help="W8A16 linear vs the bf16 GEMM at the UG-Separation page's W8A16 shapes, one JSON line each")
     ap.add_argument("--order", action="store_true",
                     help="study: contiguous vs shuffled candidate order on workloads 2-5")
     ap.add_argument("--shuffle", action="store_true",
@@ -374,6 +426,8 @@ def main():
         return order_study(args)
     if args.ugsep:
         return ugsep_study(args)
+    if args.w8a16:
+        return w8a16_study(args)
     if args.workload != 2:
         return other_workload(args)
     cfg = S.config(2)
