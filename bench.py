@@ -56,6 +56,22 @@ def glm_mlp_work(cfg, B_r, B_c):
     return F, Bts
 
 
+def step_latencies(fn, n=100):
+    """Per-step latency distribution: each step bracketed by its own events
+    on the launch stream (steps back to back, as a serving loop runs them)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.sort(np.array([e0.elapsed_time(e1) for e0, e1 in ev]))
+    return {"steps": n, "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)),
+            "max_ms": float(t[-1])}
+
+
 def time_steps(fn, steps, warmup):
     import torch
 
@@ -246,10 +262,13 @@ def regime_study(args):
         del de
         F, _ = glm_mlp_work(cfg, B_r, B_c)
         sh = t_sh / args.steps
+        st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+        lat = step_latencies(st.run, 50)
+        del st
         print(json.dumps({"study": "regime", "workload": 2, "n_per_request": n, "B_r": B_r, "B_c": B_c,
                           "shared_ms": sh * 1e3, "dense_broadcast_ms": t_de / args.steps * 1e3,
                           "speedup_vs_dense_broadcast": t_de / t_sh, "candidates_per_s": B_c / sh,
-                          "mfma_util_pct": 100.0 * F / sh / PEAK_BF16}), flush=True)
+                          "mfma_util_pct": 100.0 * F / sh / PEAK_BF16, "step_latency": lat}), flush=True)
 
 
 def order_study(args):
@@ -467,6 +486,8 @@ def main():
         "alg_flops_per_step": F,
         "alg_bytes_per_step": Bts,
     }
+    out["step_latency"] = step_latencies(shared.run)
+    log(f"bench: step latency p50 {out['step_latency']['p50_ms']:.3f} ms, p99 {out['step_latency']['p99_ms']:.3f} ms")
     if not args.no_dense:
         dense = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
         t_de, _ = time_steps(dense.run, args.steps, args.warmup)
