@@ -423,8 +423,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the ROCS stack on a single MI355X "
-              "(requests shard across GPUs with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the ROCS stack runs on a single MI355X "
+              "(requests would shard across GPUs with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

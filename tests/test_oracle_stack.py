@@ -127,7 +127,7 @@ def test_composition_closure_random_chains():
         assert np.array_equal(y1[:, :o_r], y2[:, :o_r])
 
 
-def test_full_size_batches_match_survey_counts():
+def test_full_size_batches_match_the_workload_counts():
     # the seeded count draws are part of the workload definition
     assert len(S.make_inputs(S.config(1))["cand2req"]) == 39
     for k, bc in [(2, 73704), (4, 30231), (5, 32486)]:
