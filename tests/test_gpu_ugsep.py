@@ -240,3 +240,15 @@ def test_full_size_workload_sampled():
     ref = U.ugsep_forward(inp, candidates=cand, requests=req)
     assert rel_err(y_g[cand], ref["y_g"]) <= tol("bf16")
     assert rel_err(y_u[req], ref["y_u"]) <= tol("bf16")
+
+
+def test_full_size_dense_comparator_sampled():
+    """The dense comparator (U tokens copied to every candidate) at the
+    benchmarked size, on sampled candidates: it computes the same layer."""
+    inp = S.make_ugsep_inputs(S.ugsep_config("tokenmixer"))
+    _, y_g = run_forward(inp, "bf16", 1)
+    assert np.isfinite(y_g).all()
+    B_c = len(inp["cand2req"])
+    cand = np.unique(np.concatenate([[0, B_c - 1], np.random.default_rng(2).integers(0, B_c, 14)]))
+    ref = U.ugsep_forward(inp, candidates=cand, requests=[])
+    assert rel_err(y_g[cand], ref["y_g"]) <= tol("bf16")

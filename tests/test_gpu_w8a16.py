@@ -79,6 +79,8 @@ CASES = [  # M, K, N, bias, act, padded
     (37, 384, 96, True, 0, 8),
     (64, 256, 32, False, 1, 0),
     (33, 1024, 128, True, 1, 0),
+    (64, 128, 64, True, 0, 16),  # largest M, smallest K, two output tiles, padded
+    (32, 2048, 32, False, 0, 0),  # one activation tile exactly, two blocks per wave
 ]
 
 
