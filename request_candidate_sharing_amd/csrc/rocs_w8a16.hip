@@ -66,10 +66,13 @@ __global__ __launch_bounds__(W8_NW * 64) void w8a16_kernel(W8Args a) {
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 32 + r;
       const uint4* xp = reinterpret_cast<const uint4*>(a.x + int64_t(min(m, a.M - 1)) * a.ldx + kb * W8_KB + h * 64);
+      // lanes past the last activation row load nothing (their operand is zero)
+      if (m < a.M) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 v = xp[s];
-        xb[mt][s] = m < a.M ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
+        for (int s = 0; s < 8; ++s) xb[mt][s] = __builtin_bit_cast(bf16x8, xp[s]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xb[mt][s] = bf16x8{};
       }
     }
 #pragma unroll
