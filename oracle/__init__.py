@@ -28,10 +28,11 @@ Citations name the web pages by title:
   information compensation): ``oracle/ugsep.py``; stage 4 and the W8A16
   configuration (8-bit float weights, bf16 activations): ``oracle/w8a16.py``.
 
-Parity status of every function is listed in the ``oracle/ops.py``,
-``oracle/stack.py`` and ``oracle/ugsep.py`` headers.  The two stack compositions that the pages do
-not fix (the Wukong-style layer and the ranking-scale stack) are
-"parity unpinned" beyond their building blocks.
+Pins of every function are listed in the ``oracle/ops.py``,
+``oracle/stack.py``, ``oracle/ugsep.py`` and ``oracle/w8a16.py`` headers.  The
+stack compositions are readings of the workload descriptions (the pages fix
+their operators only); each composition is pinned by special-weight closed
+forms computed with library routines.
 """
 
 from .ops import (  # noqa: F401

@@ -34,6 +34,16 @@ def _torch():
     return torch
 
 
+def encoder_depths(n_enc: int, n_int: int) -> list:
+    """Encoder output index (1..n_enc) read by each interaction layer's K/V.
+
+    Depth i of n_int pairs with encoder output ceil(i * n_enc / n_int) (the
+    ROCS review, section 2.2, pairs depth i with the i-th encoder output;
+    with fewer encoder layers the depths are spread evenly).
+    """
+    return [((i + 1) * n_enc + n_int - 1) // n_int for i in range(n_int)]
+
+
 class DeviceStack:
     """One workload's inputs, weights, descriptor and outputs on a GPU."""
 
@@ -178,7 +188,7 @@ class DeviceStack:
         for i in range(c.n_int):
             for nm in ("wk_r", "wv_r", "wk_c", "wv_c"):
                 setattr(kvw[i], nm, R.ptr(self.t(w[f"kv{i}.{nm}"])))
-        src_arr = (ctypes.c_int32 * c.n_int)(*c.depth_src())
+        src_arr = (ctypes.c_int32 * c.n_int)(*encoder_depths(c.n_enc, c.n_int))
         self._dca_arrays = (enc, kvw, src_arr)
         self.dca = R.rocs_dca_desc(c.L, dq, c.n_heads, c.ffn, c.n_enc, enc, c.n_int, src_arr, kvw)
 

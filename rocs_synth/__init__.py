@@ -8,9 +8,11 @@ arithmetic (no linear maps, norms, interactions or attention).
 Workload shapes follow the five stack configurations of the ROCS problem
 statement (liuzhao09.github.io ROCS review, section 2 "method" for the
 operators; the workload sizes themselves are the benchmark's own).  Every
-reading of an unstated detail (variance notation, fan-in, count
-distributions, which encoder depth feeds which interaction layer) is applied
-here once and documented with the configuration.
+reading of an unstated detail about the inputs (variance notation, fan-in,
+count distributions) is applied here once and documented with the
+configuration.  How the layers compose (which encoder depth feeds which
+interaction layer, for instance) is not decided here: the oracle and the
+stack descriptor each implement that reading on their own.
 
 Conventions
 -----------
@@ -112,17 +114,6 @@ class StackConfig:
 
     def with_(self, **kw) -> "StackConfig":
         return dataclasses.replace(self, **kw)
-
-    def depth_src(self) -> list:
-        """Encoder output S_k read by interaction layer i (1-based k).
-
-        Layer i of n_int reads S_ceil(i * n_enc / n_int): with two encoder
-        layers and one interaction layer that is S_2; with four interaction
-        layers it is S_1, S_1, S_2, S_2.  The pages pair depth i with S_i
-        (ROCS review, section 2.2, the DCA encoder/cross-attention equations)
-        but leave unequal depth counts open.
-        """
-        return [int(math.ceil(i * self.n_enc / self.n_int)) for i in range(1, self.n_int + 1)]
 
     def to_dict(self) -> Dict[str, Any]:
         return dataclasses.asdict(self)
