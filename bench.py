@@ -1,14 +1,17 @@
 """Throughput of the ROCS shared forward stack on one MI355X.
 
-One step = one rocs_stack_forward over one batch of the GLM MLP stack workload
-(B = 256 requests, N_b ~ U{64..512} candidates, d_R = d_C = 512, three GLM
-MLP blocks of hidden 1024 per group with residual and group-local RMSNorm,
-scalar head; bf16 storage, fp32 accumulation), inputs resident in HBM.
+One step = one rocs_stack_forward over one batch of the ranking-scale stack
+(B = 32 requests, ~1000 candidates each, a user sequence of 1024 events x 512
+with a two-layer request-only encoder, four interaction layers each a GLM MLP
+of hidden 2048 followed by DCA cross-attention to that depth's shared K/V,
+a per-candidate logit head; bf16 storage, fp32 accumulation), inputs resident
+in HBM.
 
 Prints one JSON line: candidates/s, MFMA utilisation, the same-GPU
 dense-broadcast comparator and its speedup, the roofline of the dominant
 kernel (the IKBO candidate GEMM, timed with HIP events on its launch
-stream) and the CPU oracle's rate on a bounded sample of the same batch.
+stream), the GLM MLP stack's numbers as extra keys, and the CPU oracle's
+rate on a bounded sample of the same batch.
 """
 
 from __future__ import annotations
@@ -33,32 +36,103 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def glm_mlp_costs(cfg):
+    """Per-request and per-candidate FLOPs of the GLM MLP stack ([R] §2.3:
+    C_R is paid once per request, C_C once per candidate).
+
+    Request side: each GLM linear's request GEMM [Y_R || Z] = X_R [W_RR; W_CR]^T
+    and the head's request dot.  Candidate side: X_C W_CC^T per layer and the
+    head's candidate dot."""
+    dr, dc, Hr, Hc = cfg.d_r, cfg.d_c, cfg.hid_r, cfg.hidden
+    C_R = cfg.n_blocks * (2.0 * dr * (Hr + Hc) + 2.0 * Hr * (dr + dc)) + 2.0 * dr
+    C_C = cfg.n_blocks * (2.0 * dc * Hc + 2.0 * Hc * dc) + 2.0 * dc
+    return C_R, C_C
+
+
 def glm_mlp_work(cfg, B_r, B_c):
-    """Algorithmic FLOPs and bytes of one shared-execution step (request side once, candidate side per candidate)."""
-    d, H = cfg.d_r, cfg.hidden
-    F = 0.0
+    """Algorithmic FLOPs and bytes of one shared-execution step (request side
+    once, candidate side per candidate); bytes count each kernel's operands
+    read once and outputs written once, weights once, Z (fp32) once each way."""
+    C_R, C_C = glm_mlp_costs(cfg)
+    F = B_r * C_R + B_c * C_C
+    dr, dc, Hr, Hc = cfg.d_r, cfg.d_c, cfg.hid_r, cfg.hidden
     Bts = 0.0
     for _ in range(cfg.n_blocks):
-        # up: [B_r x 2H] = x_r [W_RR; W_CR]^T ; candidates: [B_c x H] from d
-        F += 2.0 * B_r * (2 * H) * d + 2.0 * B_c * H * d
-        # down: [B_r x 2d] from H ; candidates [B_c x d] from H
-        F += 2.0 * B_r * (2 * d) * H + 2.0 * B_c * d * H
-        # bytes: activations read/written once, weights once, Z once (fp32 write + read)
-        Bts += 2 * (B_r + B_c) * d + 2 * (B_r + B_c) * H          # up: read x, write h
-        Bts += 2 * (2 * H * d + H * d)                              # up weights W_RR, W_CR, W_CC
-        Bts += 2 * 4 * B_r * H                                      # Z write + read
-        Bts += 2 * (B_r + B_c) * H + 2 * 2 * (B_r + B_c) * d        # down: read h, read residual, write o
-        Bts += 2 * (2 * d * H + d * H) + 2 * 4 * B_r * d
-        Bts += 2 * 2 * (B_r + B_c) * d                              # RMSNorm read + write
-        Bts += 4 * B_c                                              # cand2req reads
-    F += 2.0 * B_r * d + 2.0 * B_c * d                              # head
-    Bts += 2 * (B_r + B_c) * d + 4 * B_c
+        Bts += 2 * (B_r * dr + B_c * dc) + 2 * (B_r * Hr + B_c * Hc)   # up: read x, write h
+        Bts += 2 * (dr * (Hr + Hc) + dc * Hc)                           # up weights W_RR, W_CR, W_CC
+        Bts += 2 * 4 * B_r * Hc                                         # Z write + read
+        Bts += 2 * (B_r * Hr + B_c * Hc) + 2 * 2 * (B_r * dr + B_c * dc)  # down: read h, read residual, write o
+        Bts += 2 * (Hr * (dr + dc) + Hc * dc) + 2 * 4 * B_r * dc
+        Bts += 2 * 2 * (B_r * dr + B_c * dc)                            # RMSNorm read + write
+        Bts += 2 * 4 * B_c                                              # cand2req reads
+    Bts += 2 * (B_r * dr + B_c * dc) + 4 * B_c + 4 * B_c                # head: rows, map, logits
     return F, Bts
 
 
-def step_latencies(fn, n=100):
-    """Per-step latency distribution: each step bracketed by its own events
-    on the launch stream (steps back to back, as a serving loop runs them)."""
+def dca_costs(cfg):
+    """Per-request and per-candidate FLOPs of a DCA stack.  Request side
+    ([R] §2.2, request-only encoder; K/V projected once per request and
+    depth): encoder layers, K/V projections, each GLM linear's request GEMM,
+    the request queries' attention and the head's request dot.  Candidate
+    side: each GLM linear's X_C W_CC^T, the candidate query's attention over
+    L keys, the head's candidate dot."""
+    d, L, ffn, H = cfg.d_seq, cfg.L, cfg.ffn, cfg.hidden
+    enc = cfg.n_enc * (2.0 * L * d * 3 * d + 4.0 * L * L * d + 2.0 * L * d * d + 4.0 * L * d * ffn)
+    kv = cfg.n_int * 2.0 * L * d * 4 * d
+    C_R, C_C = enc + kv, 0.0
+    din_r, din_c = cfg.d_r, cfg.d_c
+    for _ in range(cfg.n_int):
+        if cfg.qgen_lcb:
+            C_R += 2.0 * din_r * (din_r + din_c)
+            C_C += 2.0 * din_c * din_c
+        C_R += 2.0 * din_r * (2 * H) + 2.0 * H * (2 * d) + 4.0 * L * d
+        C_C += 2.0 * din_c * H + 2.0 * H * d + 4.0 * L * d
+        din_r, din_c = 2 * d, 2 * d
+    if cfg.head:
+        C_R += 2.0 * din_r
+        C_C += 2.0 * din_c
+    return C_R, C_C
+
+
+def dca_work(cfg, B_r, B_c):
+    """Algorithmic FLOPs and bytes of one shared DCA stack step.  Bytes count
+    each kernel's operands read once and outputs written once (weights once,
+    Z and K/V at request size, bf16 activations, fp32 Z); the V^T staging
+    copies are not algorithmic and are left out."""
+    C_R, C_C = dca_costs(cfg)
+    F = B_r * C_R + B_c * C_C
+    d, L, ffn, H = cfg.d_seq, cfg.L, cfg.ffn, cfg.hidden
+    BL = B_r * L
+    enc = (2 * BL * d + 6 * d * d + 6 * BL * d        # QKV projection
+           + 6 * BL * d + 2 * BL * d                  # self-attention
+           + 6 * BL * d + 2 * d * d                   # out projection + residual
+           + 4 * BL * d                               # LayerNorm
+           + 2 * BL * d + 2 * ffn * d + 2 * BL * ffn  # FFN1
+           + 2 * BL * ffn + 2 * d * ffn + 4 * BL * d  # FFN2 + residual
+           + 4 * BL * d)                              # LayerNorm
+    Bts = cfg.n_enc * enc + cfg.n_int * (2 * BL * d + 8 * d * d + 8 * BL * d)
+
+    def linear(din_r, din_c, dout_r, dout_c):
+        req = 2 * B_r * din_r + 2 * din_r * (dout_r + dout_c) + 2 * B_r * dout_r + 4 * B_r * dout_c
+        cand = 2 * B_c * din_c + 2 * dout_c * din_c + 2 * B_c * dout_c + 4 * B_r * dout_c + 4 * B_c
+        return req + cand
+
+    din_r, din_c = cfg.d_r, cfg.d_c
+    for _ in range(cfg.n_int):
+        if cfg.qgen_lcb:
+            Bts += linear(din_r, din_c, din_r, din_c)
+        Bts += linear(din_r, din_c, H, H) + linear(H, H, d, d)
+        Bts += 2 * B_r * d + 4 * BL * d + 2 * B_r * d                 # request-query attention
+        Bts += 2 * B_c * d + 4 * BL * d + 2 * B_c * d + 4 * B_c       # candidate-query attention
+        din_r, din_c = 2 * d, 2 * d
+    if cfg.head:
+        Bts += 2 * (B_r * din_r + B_c * din_c) + 8 * B_c
+    return F, Bts
+
+
+def step_series(fn, n=100):
+    """Per-step GPU times (ms) of n back-to-back steps, each bracketed by its
+    own events on the launch stream (as a serving loop runs them)."""
     import torch
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -67,9 +141,28 @@ def step_latencies(fn, n=100):
         fn()
         e1.record()
     torch.cuda.synchronize()
-    t = np.sort(np.array([e0.elapsed_time(e1) for e0, e1 in ev]))
-    return {"steps": n, "p50_ms": float(np.percentile(t, 50)), "p99_ms": float(np.percentile(t, 99)),
-            "max_ms": float(t[-1])}
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+
+
+def latency_summary(t):
+    """p50 / p99 / max of a per-step series, plus what shapes its tail: the
+    share of steps more than 10 % above the median, the median of the first
+    and last quarter of the series (drift), and the lag-1 autocorrelation
+    (slow steps in runs point at a slowly varying cause such as clocks;
+    isolated ones at interference)."""
+    t = np.asarray(t, dtype=np.float64)
+    p50 = float(np.percentile(t, 50))
+    q = max(1, len(t) // 4)
+    d = t - t.mean()
+    ac = float(np.dot(d[:-1], d[1:]) / max(np.dot(d, d), 1e-30)) if len(t) > 2 else 0.0
+    return {"steps": int(len(t)), "p50_ms": p50, "p99_ms": float(np.percentile(t, 99)), "max_ms": float(t.max()),
+            "mean_ms": float(t.mean()), "frac_above_1.1x_p50": float(np.mean(t > 1.1 * p50)),
+            "first_quarter_p50_ms": float(np.median(t[:q])), "last_quarter_p50_ms": float(np.median(t[-q:])),
+            "lag1_autocorr": ac}
+
+
+def step_latencies(fn, n=100):
+    return latency_summary(step_series(fn, n))
 
 
 def time_steps(fn, steps, warmup):
@@ -89,8 +182,7 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
-ROOFLINE_KERNEL = "gemm_bf16_mixed_kernel<256, 128>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_glm_mlp.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_ranking_stack.json")
 # sources the candidate GEMM is compiled from (the counters are void once any of them changes)
 GEMM_SRCS = [os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", f)
              for f in ("rocs_gemm.hip", "rocs_mfma.h", "rocs_device.h")]
@@ -105,7 +197,7 @@ def gemm_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(alg_bytes):
+def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     only while the kernel source is the one the counters were taken on."""
     try:
@@ -117,29 +209,28 @@ def measured_traffic(alg_bytes):
     return t.get("bytes_per_launch")
 
 
-def candidate_gemm_roofline(st, reps=10, sets=3):
-    """Times the dominant kernel alone: the IKBO candidate GEMM of the GLM MLP up
-    projection (x_c [B_c, 512] -> [B_c, 1024], ReLU, Z[m_i] gathered in the
-    epilogue), launched through rocs_lcb_candidate on torch's current stream and
-    bracketed by events on that stream.  Launches rotate over `sets` buffer
-    sets (> 256 MB in total) so the Infinity Cache cannot hold the operands
-    between launches, as in the stack."""
+def candidate_gemm_roofline(batch, B_r, B_c, K, N, what, reps=10, min_set_bytes=300 << 20):
+    """Times the dominant kernel alone: one IKBO candidate GEMM
+    (x_c [B_c, K] -> [B_c, N], ReLU, Z[m_i] gathered in the epilogue) launched
+    through rocs_lcb_candidate on torch's current stream and bracketed by
+    HIP events recorded on that same stream.  Launches rotate over buffer
+    sets larger than the 256 MB Infinity Cache in total, so operands come
+    from HBM, as in the stack."""
     import torch
     from request_candidate_sharing_amd import rocs as R
 
-    cfg = st.cfg
-    B_r, B_c = st.B_r, st.B_c
-    K, N = cfg.d_r, cfg.hidden
     g = torch.Generator(device="cuda").manual_seed(0)
     bf = torch.bfloat16
     w = (torch.randn(N, K, generator=g, device="cuda") * K ** -0.5).to(bf)
     z = torch.randn(B_r, N, generator=g, device="cuda")
+    per_set = 2 * B_c * (K + N)
+    sets = max(2, -(-min_set_bytes // per_set))
     bufs = [(torch.randn(B_c, K, generator=g, device="cuda").to(bf), torch.empty(B_c, N, device="cuda", dtype=bf))
             for _ in range(sets)]
     s = R.cur_stream()
 
     def launch(b):
-        R.rocs_lcb_candidate(st.batch, R.ROCS_BF16, b[0], K, K, w, None, N, R.ROCS_ACT_RELU, z, N, None, 0, b[1],
+        R.rocs_lcb_candidate(batch, R.ROCS_BF16, b[0], K, K, w, None, N, R.ROCS_ACT_RELU, z, N, None, 0, b[1],
                              N, s)
 
     for b in bufs:
@@ -162,9 +253,10 @@ def candidate_gemm_roofline(st, reps=10, sets=3):
     else:
         rf = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
     rf["frac"] = rf["achieved"] / rf["peak"]
-    rf["traffic"] = measured_traffic(byts)
-    rf["kernel"] = ROOFLINE_KERNEL + " via rocs_lcb_candidate (GLM up projection, B_c x 512 -> B_c x 1024, Z[m_i] epilogue)"
+    rf["traffic"] = measured_traffic()
+    rf["kernel"] = what
     rf["avg_launch_us"] = t * 1e6
+    rf["launches_timed"] = reps * sets
     rf["alg_flops_per_launch"] = flops
     rf["alg_bytes_per_launch"] = byts
     rf["mfma_frac"] = flops / t / PEAK_BF16
@@ -195,11 +287,33 @@ def oracle_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(inp, seconds):
+def cpu_baseline(inp, seconds, max_cands=None):
+    """The oracle on whole requests of the same batch until about ``seconds``
+    of CPU time.  ``max_cands`` caps the sample at the first candidates of
+    the first request instead (a request of the ranking-scale stack alone
+    takes longer than the bound); the oracle's cost is per candidate, so
+    candidates/s is unchanged by the cap."""
     import oracle
+    import rocs_synth as S
 
     threads = oracle_threads()
     counts = inp["counts"]
+    if max_cands is not None:
+        b = int(np.nonzero(counts)[0][0])
+        n = min(int(counts[b]), max_cands)
+        sub = dict(inp)
+        keep = np.zeros(len(counts), dtype=np.int64)
+        keep[b] = n
+        sub.update(S.make_batch(keep))
+        o = int(inp["offsets"][b])
+        sub["x_c"] = inp["x_c"][o:o + n]
+        t0 = time.perf_counter()
+        oracle.oracle_forward(sub, requests=[b])
+        el = time.perf_counter() - t0
+        return {"value": n / el, "unit": "candidates/s", "cores": threads, "kind": "oracle",
+                "sample": f"float64 numpy oracle (dense masked model, materialized broadcast) on request {b} "
+                          f"of the same batch, its first {n} of {int(counts[b])} candidates (the request's "
+                          f"sequence encoder included): {n} candidates in {el:.1f} s"}
     done, n_req, t_total = 0, 0, 0.0
     for b in range(len(counts)):
         if counts[b] == 0:
@@ -241,34 +355,42 @@ def other_workload(args):
     print(json.dumps(out), flush=True)
 
 
-def regime_study(args):
-    """Shared vs dense-broadcast step time on the GLM MLP stack shapes with a
-    fixed number of candidates per request, N in {1, 10, 100, 500, 1000}
-    (256 requests): the regime in which request sharing pays, and the
-    N = 500 ratio check."""
+def rrr_study(args):
+    """Request-oriented resource reallocation ([R] §2.3): the GLM MLP stack
+    with its request-side path r times as wide (d_R = r 512, hidden_R =
+    r 1024; candidate side fixed) at N fixed candidates per request.  For
+    each (r, N): the FLOP accounting of the page (C_R once per request, C_C
+    per candidate, FLOPs@1 = C_R + C_C, FLOPs@100 = C_C + C_R/100, C_amort(N)
+    = C_C + C_R/N), the measured shared and dense-broadcast step times, the
+    measured time per candidate, and the step-latency distribution."""
     import rocs_synth as S
     from request_candidate_sharing_amd import rocs as R
     from request_candidate_sharing_amd.stacks import DeviceStack
 
-    cfg = S.config(2)
-    for n in (1, 10, 100, 500, 1000):
-        inp = S.make_inputs(cfg, counts=[n] * cfg.B)
-        B_r, B_c = cfg.B, int(len(inp["cand2req"]))
-        st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
-        t_sh, _ = time_steps(st.run, args.steps, args.warmup)
-        del st
-        de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
-        t_de, _ = time_steps(de.run, args.steps, args.warmup)
-        del de
-        F, _ = glm_mlp_work(cfg, B_r, B_c)
-        sh = t_sh / args.steps
-        st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
-        lat = step_latencies(st.run, 50)
-        del st
-        print(json.dumps({"study": "regime", "workload": 2, "n_per_request": n, "B_r": B_r, "B_c": B_c,
-                          "shared_ms": sh * 1e3, "dense_broadcast_ms": t_de / args.steps * 1e3,
-                          "speedup_vs_dense_broadcast": t_de / t_sh, "candidates_per_s": B_c / sh,
-                          "mfma_util_pct": 100.0 * F / sh / PEAK_BF16, "step_latency": lat}), flush=True)
+    rs = [int(x) for x in args.rrr_r.split(",")]
+    ns = [int(x) for x in args.rrr_n.split(",")]
+    for r in rs:
+        for n in ns:
+            cfg = S.rrr_config(r, n)
+            inp = S.make_inputs(cfg)
+            B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+            C_R, C_C = glm_mlp_costs(cfg)
+            out = {"study": "rrr", "r": r, "n_per_request": n, "B_r": B_r, "B_c": B_c, "d_R": cfg.d_r,
+                   "hidden_R": cfg.hid_r, "d_C": cfg.d_c, "hidden_C": cfg.hidden,
+                   "C_R_flops": C_R, "C_C_flops": C_C, "C_R_over_C_C": C_R / C_C,
+                   "flops_at_1": C_R + C_C, "flops_at_100": C_C + C_R / 100.0, "C_amort_N": C_C + C_R / n}
+            st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+            t_sh, _ = time_steps(st.run, args.steps, args.warmup)
+            sh = t_sh / args.steps
+            out.update(shared_ms=sh * 1e3, us_per_candidate=sh * 1e6 / B_c, candidates_per_s=B_c / sh)
+            out["step_latency"] = latency_summary(step_series(st.run, args.latency_steps))
+            del st
+            if not args.no_dense:
+                de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+                t_de, _ = time_steps(de.run, args.steps, args.warmup)
+                del de
+                out.update(dense_broadcast_ms=t_de / args.steps * 1e3, speedup_vs_dense_broadcast=t_de / t_sh)
+            print(json.dumps(out), flush=True)
 
 
 def order_study(args):
@@ -398,6 +520,35 @@ def w8a16_study(args):
         del wq, wb
 
 
+def glm_stack_line(args):
+    """The GLM MLP stack (B_r = 256, U{64..512} candidates per request, d 512,
+    three blocks of hidden 1024) in the shared and dense-broadcast modes:
+    extra keys of the headline line."""
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    cfg = S.config(2)
+    inp = S.make_inputs(cfg)
+    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+    st = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+    t_sh, _ = time_steps(st.run, args.steps, args.warmup)
+    sh = t_sh / args.steps
+    F, Bts = glm_mlp_work(cfg, B_r, B_c)
+    out = {"workload": "GLM MLP stack: B_r=256, candidates/request ~U{64..512} (B_c=%d), d_R=d_C=512, 3 GLM MLP "
+                       "blocks (hidden 1024 per group) + residual + group RMSNorm, scalar head" % B_c,
+           "B_r": B_r, "B_c": B_c, "ms_per_step": sh * 1e3, "candidates_per_s": B_c / sh,
+           "mfma_util_pct": 100.0 * F / sh / PEAK_BF16, "hbm_util_pct": 100.0 * Bts / sh / PEAK_HBM}
+    del st
+    if not args.no_dense:
+        de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+        t_de, _ = time_steps(de.run, args.steps, args.warmup)
+        del de
+        out["dense_broadcast_ms_per_step"] = t_de / args.steps * 1e3
+        out["speedup_vs_dense_broadcast"] = t_de / t_sh
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,13 +556,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-broadcast comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-glm", action="store_true", help="skip the GLM MLP stack extra keys")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-cands", type=int, default=256,
+                    help="candidates of one request the CPU oracle evaluates for the ranking-scale stack")
     ap.add_argument("--roofline-reps", type=int, default=10)
+    ap.add_argument("--steady-steps", type=int, default=100,
+                    help="steps of the steady-state window timed after the contract's timed steps")
+    ap.add_argument("--latency-steps", type=int, default=100)
     ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
-    ap.add_argument("--workload", type=int, default=2,
-                    help="profiling aid: time another workload's stack (1-5); the benchmark line is workload 2")
-    ap.add_argument("--regime", action="store_true",
-                    help="study: shared vs dense broadcast at N = 1..1000 candidates per request (workload 2 shapes)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="5 (default) is the benchmark line; 1-4 time another workload's stack (profiling aid)")
+    ap.add_argument("--rrr", action="store_true",
+                    help="study: request-side scaling r x candidates per request N on the GLM MLP stack shapes")
+    ap.add_argument("--rrr-r", default="1,2,4")
+    ap.add_argument("--rrr-n", default="1,10,100,500,1000")
     ap.add_argument("--ugsep", action="store_true",
                     help="the UG-Separation TokenMixer workload (shared vs dense comparator), one JSON line")
     ap.add_argument("--w8a16", action="store_true",
@@ -419,7 +578,7 @@ def main():
     ap.add_argument("--order", action="store_true",
                     help="study: contiguous vs shuffled candidate order on workloads 2-5")
     ap.add_argument("--shuffle", action="store_true",
-                    help="with --workload k (k != 2): candidates in one random global order (offsets NULL)")
+                    help="with --workload k (k != 5): candidates in one random global order (offsets NULL)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -439,28 +598,37 @@ def main():
     from request_candidate_sharing_amd.stacks import DeviceStack
 
     torch.cuda.set_device(0)
-    if args.regime:
-        return regime_study(args)
+    if args.rrr:
+        return rrr_study(args)
     if args.order:
         return order_study(args)
     if args.ugsep:
         return ugsep_study(args)
     if args.w8a16:
         return w8a16_study(args)
-    if args.workload != 2:
+    if args.workload != 5:
         return other_workload(args)
-    cfg = S.config(2)
+
+    cfg = S.config(5)
     inp = S.make_inputs(cfg)
     B_r, B_c = cfg.B, int(len(inp["cand2req"]))
     log(f"bench: {cfg.name()} B_r={B_r} B_c={B_c}")
-
+    F, Bts = dca_work(cfg, B_r, B_c)
     shared = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED)
+    dense_out = None
+    if not args.no_dense:
+        # the comparator runs first, so the shared steps below start on a busy, clocked-up GPU
+        dense = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
+        t_de, _ = time_steps(dense.run, args.steps, args.warmup)
+        dense_out = {"value": B_c * args.steps / t_de, "ms_per_step": t_de / args.steps * 1e3}
+        log(f"bench: dense broadcast {t_de / args.steps * 1e3:.3f} ms/step")
+        del dense
+
     t_sh, wall_sh = time_steps(shared.run, args.steps, args.warmup)
     ms = t_sh / args.steps * 1e3
     value = B_c * args.steps / t_sh
-    log(f"bench: shared {ms:.3f} ms/step, {value:.4g} candidates/s (wall {wall_sh:.3f} s)")
-    F, Bts = glm_mlp_work(cfg, B_r, B_c)
     step_s = t_sh / args.steps
+    log(f"bench: shared {ms:.3f} ms/step, {value:.4g} candidates/s (wall {wall_sh:.3f} s)")
 
     out = {
         "metric": METRIC,
@@ -474,32 +642,45 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) features, N(0,1/fan_in) weights)",
+        "data": "synthetic (seeded N(0,1) features and sequences, N(0,1/fan_in) weights)",
         "config": {
-            "workload": "GLM MLP stack: B_r=256 requests, candidates/request ~U{64..512} (B_c=%d), d_R=d_C=512, "
-                        "3 GLM MLP blocks (hidden 1024 per group, ReLU) + residual + group-local RMSNorm, "
-                        "scalar GLM head; bf16 storage, fp32 accumulate" % B_c,
-            "B_r": B_r, "B_c": B_c, "global_batch": B_c, "seq_len": 0, "parallelism": "single GPU",
+            "workload": "ranking-scale full stack: B_r=32 requests, ~1000 candidates/request (log-normal +-30%%, "
+                        "B_c=%d), user sequence L=1024 x d=512 with a 2-layer request-only encoder (8 heads), "
+                        "4 interaction layers each a GLM MLP of hidden 2048 (d_R=d_C=512) + DCA cross-attention "
+                        "to that depth's shared K/V, per-candidate logit head; bf16 storage, fp32 accumulate" % B_c,
+            "B_r": B_r, "B_c": B_c, "global_batch": B_c, "seq_len": cfg.L, "parallelism": "single GPU",
         },
         "mfma_util_pct": 100.0 * F / step_s / PEAK_BF16,
         "hbm_util_pct": 100.0 * Bts / step_s / PEAK_HBM,
         "alg_flops_per_step": F,
         "alg_bytes_per_step": Bts,
     }
-    out["step_latency"] = step_latencies(shared.run)
-    log(f"bench: step latency p50 {out['step_latency']['p50_ms']:.3f} ms, p99 {out['step_latency']['p99_ms']:.3f} ms")
-    if not args.no_dense:
-        dense = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
-        t_de, _ = time_steps(dense.run, args.steps, args.warmup)
-        out["dense_broadcast"] = {"value": B_c * args.steps / t_de, "ms_per_step": t_de / args.steps * 1e3}
-        out["speedup_vs_dense_broadcast"] = t_de / t_sh
-        log(f"bench: dense broadcast {t_de / args.steps * 1e3:.3f} ms/step, speedup {t_de / t_sh:.3f}x")
-        del dense
-    out["roofline"] = candidate_gemm_roofline(shared, args.roofline_reps)
+    if dense_out is not None:
+        out["dense_broadcast"] = dense_out
+        out["speedup_vs_dense_broadcast"] = dense_out["ms_per_step"] / ms
+        log(f"bench: speedup vs dense broadcast {out['speedup_vs_dense_broadcast']:.2f}x")
+    if args.steady_steps > 0:
+        t_st, _ = time_steps(shared.run, args.steady_steps, 0)
+        out["steady_state"] = {"steps": args.steady_steps, "ms_per_step": t_st / args.steady_steps * 1e3,
+                               "candidates_per_s": B_c * args.steady_steps / t_st}
+        log(f"bench: steady state {t_st / args.steady_steps * 1e3:.3f} ms/step over {args.steady_steps} steps")
+    if args.latency_steps > 0:
+        out["step_latency"] = step_latencies(shared.run, args.latency_steps)
+        log(f"bench: step latency p50 {out['step_latency']['p50_ms']:.3f} ms, "
+            f"p99 {out['step_latency']['p99_ms']:.3f} ms")
+    K, N = 2 * cfg.d_seq, cfg.hidden
+    out["roofline"] = candidate_gemm_roofline(
+        shared.batch, B_r, B_c, K, N,
+        "gemm_bf16_big_kernel<256, 256, 2, 4, 2> via rocs_lcb_candidate (interaction-layer MLP1 of the ranking "
+        "stack, layers 2-4: B_c x 1024 -> B_c x 2048, ReLU, Z[m_i] epilogue)", args.roofline_reps)
     log(f"bench: candidate GEMM {out['roofline']['avg_launch_us']:.1f} us/launch, "
         f"{out['roofline']['achieved']:.1f} {out['roofline']['unit']} ({out['roofline']['frac']:.3f} of peak)")
+    del shared
+    if not args.no_glm:
+        out["glm_mlp_stack"] = glm_stack_line(args)
+        log(f"bench: GLM MLP stack {out['glm_mlp_stack']['ms_per_step']:.3f} ms/step")
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, max_cands=args.cpu_cands)
         log(f"bench: cpu oracle {out['cpu_baseline']['value']:.4g} candidates/s")
     print(json.dumps(out), flush=True)
 

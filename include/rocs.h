@@ -247,7 +247,12 @@ int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* 
  * slots >= 2 are carved from the workspace with 16-byte-padded rows.  Each
  * slot has a request part [B_r, width_r] and a candidate part
  * [B_c, width_c].  Layers read and write column ranges of slots, so a
- * concatenation is two layers writing adjacent columns of one slot. */
+ * concatenation is two layers writing adjacent columns of one slot.
+ * A layer's output view may not overlap the views it reads (tiles would
+ * overwrite rows other tiles still read), with two element-wise
+ * exceptions: a NORM may run in place (src view == dst view), and a
+ * residual view may equal the output view.  Other overlaps are rejected
+ * with ROCS_ERR_INVALID_ARG before anything is enqueued. */
 typedef enum rocs_exec_mode {
   ROCS_EXEC_SHARED = 0,         /* request work at B_r size, map resolved in-kernel */
   ROCS_EXEC_DENSE_BROADCAST = 1 /* comparator: request contributions and K/V copied to B_c rows first */

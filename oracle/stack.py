@@ -126,9 +126,10 @@ def _forward_rows(cfg, w, x_r_rows, x_c_rows, req_of, enc) -> Dict[str, np.ndarr
 
     if cfg.kind == "glm_mlp":
         x = np.concatenate([x_r_rows, x_c_rows], axis=1)
+        Hr = cfg.hidden_r or H  # request-group hidden width (request-side scaling, [R] §2.3)
         for k in range(cfg.n_blocks):
-            h = ops.relu(ops.glm_linear(x, w[f"blk{k}.up.W"], w[f"blk{k}.up.b"], cfg.d_r, H))
-            o = ops.glm_linear(h, w[f"blk{k}.down.W"], w[f"blk{k}.down.b"], H, cfg.d_r)
+            h = ops.relu(ops.glm_linear(x, w[f"blk{k}.up.W"], w[f"blk{k}.up.b"], cfg.d_r, Hr))
+            o = ops.glm_linear(h, w[f"blk{k}.down.W"], w[f"blk{k}.down.b"], Hr, cfg.d_r)
             x = ops.group_norm(x + o, [cfg.d_r, cfg.d_c], "rms", cfg.eps)
         logits = ops.glm_linear(x, w["head.W"], w["head.b"], cfg.d_r, 0)[:, 0]
         return {"y": x, "w_r": cfg.d_r, "logits": logits}

@@ -143,7 +143,7 @@ class DeviceStack:
 
     def _build_glm_mlp(self):
         c, w = self.cfg, self.inputs["w"]
-        d, H = (c.d_r, c.d_c), (c.hidden, c.hidden)
+        d, H = (c.d_r, c.d_c), (c.hidden_r or c.hidden, c.hidden)
         s0 = self.slot(*d)
         s1 = self.slot(*d)
         sh = self.slot(*H)

@@ -40,6 +40,7 @@ __all__ = [
     "StackConfig",
     "config",
     "small_config",
+    "rrr_config",
     "make_inputs",
     "make_batch",
     "shuffle_candidates",
@@ -89,7 +90,8 @@ class StackConfig:
     counts: tuple  # ("uniform", lo, hi) | ("fixed", n) | ("lognormal", median, sigma, lo, hi)
     d_r: int = 0
     d_c: int = 0
-    hidden: int = 0  # per-group hidden width of the GLM MLPs
+    hidden: int = 0  # hidden width of the GLM MLPs (candidate group; request group too unless hidden_r)
+    hidden_r: int = 0  # request-group hidden width when it differs (request-side scaling r)
     n_blocks: int = 0  # glm_mlp: residual MLP blocks
     # DCA
     L: int = 0
@@ -111,6 +113,11 @@ class StackConfig:
 
     def name(self) -> str:
         return CONFIG_NAMES.get(self.key, self.kind)
+
+    @property
+    def hid_r(self) -> int:
+        """Request-group hidden width of the GLM MLP blocks."""
+        return self.hidden_r or self.hidden
 
     def with_(self, **kw) -> "StackConfig":
         return dataclasses.replace(self, **kw)
@@ -142,6 +149,19 @@ def config(k: int) -> StackConfig:
                            d_r=512, d_c=512, hidden=2048, L=1024, d_seq=512, n_heads=8, head_dim=64,
                            ffn=2048, n_enc=2, n_int=4, qgen_lcb=False, head=True)
     raise ValueError(f"no configuration {k}")
+
+
+def rrr_config(r: int, n: Optional[int] = None) -> StackConfig:
+    """The GLM MLP stack with the request-side path r times as wide.
+
+    Request-oriented resource reallocation (ROCS review, section 2.3) scales
+    the request-side width of every module by r: d_R = r * 512 and the
+    request-group hidden width r * 1024, the candidate side unchanged.
+    ``n`` fixes the candidates per request (otherwise U{64..512}).
+    """
+    c = config(2)
+    counts = ("fixed", n) if n is not None else c.counts
+    return c.with_(d_r=r * c.d_r, hidden_r=r * c.hidden, counts=counts)
 
 
 def small_config(k: int) -> StackConfig:
@@ -241,9 +261,9 @@ def make_inputs(cfg: StackConfig, seed: Optional[int] = None, counts=None) -> Di
         w["lin.b"] = zeros(2 * cfg.hidden)
     elif cfg.kind == "glm_mlp":
         for k in range(cfg.n_blocks):
-            w[f"blk{k}.up.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, cfg.hidden, cfg.hidden, bf16)
-            w[f"blk{k}.up.b"] = zeros(2 * cfg.hidden)
-            w[f"blk{k}.down.W"] = glm_weight(rng, cfg.hidden, cfg.hidden, cfg.d_r, cfg.d_c, bf16)
+            w[f"blk{k}.up.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, cfg.hid_r, cfg.hidden, bf16)
+            w[f"blk{k}.up.b"] = zeros(cfg.hid_r + cfg.hidden)
+            w[f"blk{k}.down.W"] = glm_weight(rng, cfg.hid_r, cfg.hidden, cfg.d_r, cfg.d_c, bf16)
             w[f"blk{k}.down.b"] = zeros(cfg.d_r + cfg.d_c)
         w["head.W"] = glm_weight(rng, cfg.d_r, cfg.d_c, 0, 1, bf16)
         w["head.b"] = zeros(1)

@@ -147,6 +147,37 @@ def test_stack_descriptor_errors():
     assert st == R.ROCS_ERR_INVALID_ARG
 
 
+def test_stack_rejects_overlapping_views():
+    # A LINEAR whose output columns overlap its input columns in one slot
+    # would race between tiles: rejected.  A NORM in place and a residual
+    # equal to the output view are element-wise and stay legal.
+    desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
+    assert R.rocs_stack_workspace_size(desc, 2, 6) > 0
+    layers = desc.layers
+    up = layers[0]
+    up.dst, up.dst_col_r, up.dst_col_c = 2, 0, 0
+    up.src = 2  # reads the slot it writes
+    up.d_in_r = up.d_in_c = 128
+    assert R.rocs_stack_workspace_size(desc, 2, 6) == 0
+    assert "overlaps" in R.last_error()
+    # disjoint columns of the same slot are fine: [0, 128) -> [128, 256) is not possible here
+    # (the output is 256 wide), so check a partial residual overlap instead
+    desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
+    down = desc.layers[1]
+    down.res, down.res_col_r, down.res_col_c = 3, 0, 0  # the output view itself: allowed
+    assert R.rocs_stack_workspace_size(desc, 2, 6) > 0
+    desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
+    down = desc.layers[1]
+    desc.slots[3].width_r = desc.slots[3].width_c = 256
+    down.res, down.res_col_r, down.res_col_c = 3, 64, 64  # shifted by 64 columns: a race
+    assert R.rocs_stack_workspace_size(desc, 2, 6) == 0
+    assert "overlaps" in R.last_error()
+    desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
+    norm = desc.layers[2]
+    norm.src = norm.dst = 3  # in place: allowed
+    assert R.rocs_stack_workspace_size(desc, 2, 6) > 0
+
+
 def test_stack_forward_checks_workspace_before_launch():
     desc = _glm_mlp_desc(d=128, H=256, n_blocks=1)
     io = R.rocs_stack_io(FAKE, 128, FAKE, 128, FAKE, 128, FAKE, 128, None, FAKE)

@@ -117,6 +117,18 @@ def test_fused_mlp_block_matches_unfused_layers(k):
         assert np.array_equal(a["y_c"], b["y_c"])
 
 
+@pytest.mark.parametrize("r", [2, 3])
+def test_request_side_scaled_stack_parity(r):
+    # Request-side scaling r ([R] §2.3): the GLM MLP stack with request
+    # widths d_R = r d and hidden_R = r H, candidate widths unchanged.
+    c = S.small_config(2)
+    cfg = c.with_(d_r=r * c.d_r, hidden_r=r * c.hidden)
+    inp = S.make_inputs(cfg)
+    _, got = _stack(inp)
+    assert got["y_r"].shape == (cfg.B, r * c.d_r)
+    _compare(cfg, got, oracle.oracle_forward(inp))
+
+
 def test_single_candidate_requests_match_oracle():
     cfg = S.small_config(2)
     inp = S.make_inputs(cfg, counts=[1] * cfg.B)

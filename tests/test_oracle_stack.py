@@ -231,10 +231,13 @@ def test_glm_tiny_identity_weights_give_relu_of_group_layernorm():
     _close(out["y_c"], np.maximum(_ln(xc), 0.0))
 
 
-def test_glm_mlp_zero_down_projection_gives_repeated_rmsnorm_and_head_dots():
+@pytest.mark.parametrize("r", [1, 2])
+def test_glm_mlp_zero_down_projection_gives_repeated_rmsnorm_and_head_dots(r):
     # o = 0, so every block is x <- RMSNorm_g(x + 0): n_blocks nested rms_norms
-    # per group; the head is then w_CR . y_R[m] + w_CC . y_C.
+    # per group; the head is then w_CR . y_R[m] + w_CC . y_C.  r = 2 widens the
+    # request-side path (request-side scaling, [R] §2.3).
     cfg = S.small_config(2)
+    cfg = cfg.with_(d_r=r * cfg.d_r, hidden_r=r * cfg.hidden)
     inp = S.make_inputs(cfg)
     w = inp["w"]
     for k in range(cfg.n_blocks):
@@ -412,7 +415,7 @@ def test_planted_norm_kind_swap_fails_the_rmsnorm_pin(monkeypatch):
 
     monkeypatch.setattr(ops, "group_norm", swapped)
     with pytest.raises(AssertionError):
-        test_glm_mlp_zero_down_projection_gives_repeated_rmsnorm_and_head_dots()
+        test_glm_mlp_zero_down_projection_gives_repeated_rmsnorm_and_head_dots(1)
 
 
 def test_planted_attention_group_swap_fails_the_one_event_pin(monkeypatch):
