@@ -166,9 +166,9 @@ template <int FN, int JWM = 2>
 __device__ __forceinline__ int stage_at(int r, int c) { return r * stage_pitch<FN, JWM>() + c; }
 
 // Epilogue variants.  EPI_ANY tests every optional term at run time; the
-// others are fixed at compile time for the candidate GEMMs of the layer
-// stacks (request contribution gathered through the map, bias, then ReLU or
-// a residual), with 32-bit row offsets (launch_gemm checks the ranges).
+// others are fixed at compile time (request contribution gathered through
+// the map or none, bias or none, then ReLU, a residual or neither), with
+// 32-bit row offsets (launch_gemm checks the ranges).
 enum : int {
   EPI_ANY = 0,
   EPI_Z = 1,     // z with zmap
@@ -176,6 +176,7 @@ enum : int {
   EPI_RELU = 4,
   EPI_RES = 8,
   EPI_ZACC = 16,  // with EPI_Z: the tile's accumulators started at Z[m_i] (zinit_acc)
+  EPI_SPEC = 32,  // without EPI_Z: a fixed variant with no request contribution
 };
 
 // Writes one 32-row block-row of a wave's tile through the epilogue.  Block
@@ -331,18 +332,19 @@ __device__ __forceinline__ void store_blocks_as(const GemmArgs& a, int mb, int n
 template <int JWM = 2, int FM, int FN>
 __device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, const f32x16 (&acc)[FM][FN],
                                              float* stage) {
-  constexpr int ZA = EPI_Z | EPI_ZACC;
+#define ROCS_EPI_CASE(V) \
+  case (V): store_blocks_as<(V), JWM>(a, mb, nb, lane, acc, stage); break;
+#define ROCS_EPI_TAILS(P) \
+  ROCS_EPI_CASE(P) ROCS_EPI_CASE(P | EPI_RELU) ROCS_EPI_CASE(P | EPI_RES) ROCS_EPI_CASE(P | EPI_BIAS) \
+  ROCS_EPI_CASE(P | EPI_BIAS | EPI_RELU) ROCS_EPI_CASE(P | EPI_BIAS | EPI_RES)
   switch (a.epi) {
-    case EPI_Z | EPI_BIAS | EPI_RELU: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_BIAS | EPI_RES: store_blocks_as<EPI_Z | EPI_BIAS | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_RELU: store_blocks_as<EPI_Z | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
-    case EPI_Z | EPI_RES: store_blocks_as<EPI_Z | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
-    case ZA | EPI_BIAS | EPI_RELU: store_blocks_as<ZA | EPI_BIAS | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
-    case ZA | EPI_BIAS | EPI_RES: store_blocks_as<ZA | EPI_BIAS | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
-    case ZA | EPI_RELU: store_blocks_as<ZA | EPI_RELU, JWM>(a, mb, nb, lane, acc, stage); break;
-    case ZA | EPI_RES: store_blocks_as<ZA | EPI_RES, JWM>(a, mb, nb, lane, acc, stage); break;
+    ROCS_EPI_TAILS(EPI_Z)
+    ROCS_EPI_TAILS(EPI_Z | EPI_ZACC)
+    ROCS_EPI_TAILS(EPI_SPEC)
     default: store_blocks_as<EPI_ANY, JWM>(a, mb, nb, lane, acc, stage); break;
   }
+#undef ROCS_EPI_TAILS
+#undef ROCS_EPI_CASE
 }
 
 // ----------------------------------------------------------------- DMA-staged bf16 GEMM
@@ -734,28 +736,23 @@ hipError_t launch_mixed(const GemmArgs& a, int M1, int h2, int grid, hipStream_t
 }
 
 // Epilogue variant of a launch: one of the specialised ones when the terms
-// match and every offset fits 32 bits, else EPI_ANY.
+// match (at most one of ReLU and a residual) and every offset fits 32 bits,
+// else EPI_ANY.
 int epilogue_variant(const GemmArgs& a) {
-  if (a.z == nullptr || a.out0_f32 || a.act > 1) return EPI_ANY;
+  if (a.out0_f32 || a.act > 1 || (a.act == 1 && a.res != nullptr)) return EPI_ANY;
   const int64_t lim = int64_t(1) << 31;
-  if (int64_t(a.zrows) * a.ldz >= lim || int64_t(a.M) * a.ld0 >= lim) return EPI_ANY;
+  if (int64_t(a.M) * a.ld0 >= lim) return EPI_ANY;
   if (a.res != nullptr && int64_t(a.M) * a.ldres >= lim) return EPI_ANY;
+  const int tail = (a.bias ? EPI_BIAS : 0) | (a.act == 1 ? EPI_RELU : 0) | (a.res ? EPI_RES : 0);
+  if (a.z == nullptr) return EPI_SPEC | tail;
+  if (int64_t(a.zrows) * a.ldz >= lim) return EPI_ANY;
   // Z goes into the accumulators at tile start when no tile takes the edge
   // path (which adds Z itself): N a multiple of every tile width, one output.
   // Mapped and unmapped Z (the dense-broadcast comparator's copied rows) then
   // sum in the same order.
   const bool zacc = a.N % 256 == 0 && a.n_split >= a.N;
   if (a.zmap == nullptr && !zacc) return EPI_ANY;
-  const int v = EPI_Z | (a.bias ? EPI_BIAS : 0) | (a.act == 1 ? EPI_RELU : 0) | (a.res ? EPI_RES : 0);
-  switch (v) {
-    case EPI_Z | EPI_BIAS | EPI_RELU:
-    case EPI_Z | EPI_BIAS | EPI_RES:
-    case EPI_Z | EPI_RELU:
-    case EPI_Z | EPI_RES:
-      return zacc ? v | EPI_ZACC : v;
-    default:
-      return EPI_ANY;
-  }
+  return EPI_Z | tail | (zacc ? EPI_ZACC : 0);
 }
 
 // bf16 launches below the candidate-size threshold that take the split-K
