@@ -233,6 +233,26 @@ int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_hea
                         const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv, float scale, void* a_r,
                         int64_t ld_ar, void* a_c, int64_t ld_ac, void* workspace, size_t ws_bytes, void* stream);
 
+/* Variant of rocs_dca_cross_attn that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as rocs_dca_cross_attn except:
+ * - its only scratch, the attention plan (per-request counts and offsets,
+ *   the candidate permutation, the query tiles), lives in a static device
+ *   array of ROCS_XATTN_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ *   process ends; a batch whose plan needs more (about 4 bytes per
+ *   candidate plus 24 bytes per request) returns ROCS_ERR_WORKSPACE before
+ *   anything is enqueued;
+ * - V is transposed inside the attention kernel instead of being staged.
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (each call clears what must start at zero).  Calls that
+ * overlap on one GPU (other streams, other host threads) race. */
+#define ROCS_XATTN_NOALLOC_SCRATCH_BYTES (4 << 20)
+int rocs_dca_cross_attn_noalloc(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim,
+                                int32_t L, const void* q_r, int64_t ld_qr, const void* q_c, int64_t ld_qc,
+                                const void* k_r, const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv,
+                                float scale, void* a_r, int64_t ld_ar, void* a_c, int64_t ld_ac, void* stream);
+
 /* ------------------------------------------------------------------ explicit broadcast (comparator)
  * dst row i = src row m_i, copied byte for byte (the materialized broadcast
  * of [R] §2.4, Figure 3(a); used only by the dense-broadcast comparator).

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -14,6 +15,9 @@
 #include "rocs_internal.h"
 
 using namespace rocs;
+
+// Static device scratch of rocs_dca_cross_attn_noalloc (see noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[ROCS_XATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -504,6 +508,30 @@ int xattn_candidate_launch(int B_r, int B_c, const XattnPlan& plan, int H, int L
   return ROCS_OK;
 }
 
+// Scratch of rocs_dca_cross_attn_noalloc: a static device array (one copy per
+// GPU, held until the process ends).  Host code never passes the array's
+// name to a kernel (in host code that name is not a device address): each
+// device's address comes from hipGetSymbolAddress, called once per device
+// with that device current, and kernels receive that pointer.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out, const char* fn) {
+  int dev = 0;
+  ROCS_HIP(hipGetDevice(&dev), fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(ROCS_ERR_UNSUPPORTED, "%s: device index %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    ROCS_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), fn);
+    if (!p) return fail(ROCS_ERR_HIP, "%s: no device address for the static scratch", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ROCS_OK;
+}
+
 float scale_log2_of(float scale) {
   const float sc = scale > 0.f ? scale : 0.125f;
   return sc * 1.4426950408889634f;
@@ -832,6 +860,35 @@ int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* 
   ROCS_HIP(launch_broadcast_rows(batch->num_candidates, batch->cand2req, batch->num_requests, row_bytes, src,
                                  src_stride, dst, dst_stride, as_stream(stream)),
            fn);
+  return ok();
+}
+
+int rocs_dca_cross_attn_noalloc(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim,
+                                int32_t L, const void* q_r, int64_t ld_qr, const void* q_c, int64_t ld_qc,
+                                const void* k_r, const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv,
+                                float scale, void* a_r, int64_t ld_ar, void* a_c, int64_t ld_ac, void* stream) {
+  const char* fn = "rocs_dca_cross_attn_noalloc";
+  ROCS_TRY(xattn_check(batch, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld_qc, k_r, v_r, k_c, v_c, ld_kv, a_r,
+                       ld_ar, a_c, ld_ac, fn));
+  const int B_r = batch->num_requests, B_c = batch->num_candidates;
+  // the attention plan is the only scratch: V is transposed inside the attention kernel
+  const size_t need = B_c > 0 ? xattn_plan_bytes(B_r, B_c) : 0;
+  if (need > ROCS_XATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(ROCS_ERR_WORKSPACE, "%s: the attention plan of %d requests and %d candidates needs %zu bytes, more "
+                "than the %d-byte static scratch", fn, B_r, B_c, need, int(ROCS_XATTN_NOALLOC_SCRATCH_BYTES));
+  hipStream_t s = as_stream(stream);
+  const float sl2 = scale_log2_of(scale);
+  ROCS_TRY(xattn_request_launch(B_r, n_heads, L, q_r, ld_qr, k_r, v_r, ld_kv, sl2, a_r, ld_ar, nullptr, s));
+  if (B_c > 0) {
+    void* scratch = nullptr;
+    ROCS_TRY(noalloc_scratch(&scratch, fn));
+    XattnPlan p;
+    ROCS_HIP(launch_attn_plan(B_r, B_c, batch->offsets, batch->cand2req, scratch, &p.tiles, &p.n_tiles, &p.perm,
+                              &p.max_tiles, s),
+             fn);
+    ROCS_TRY(xattn_candidate_launch(B_r, B_c, p, n_heads, L, q_c, ld_qc, k_c, v_c, ld_kv, int64_t(L) * ld_kv, sl2,
+                                    a_c, ld_ac, nullptr, s));
+  }
   return ok();
 }
 

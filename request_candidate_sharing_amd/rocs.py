@@ -142,6 +142,8 @@ _SIGS = {
     "rocs_dca_cross_attn_workspace_size": [c_int32, c_int32, c_int32, c_int32],
     "rocs_dca_cross_attn": [P, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, P, P, c_int64,
                             c_float, P, c_int64, P, c_int64, P, c_size_t, P],
+    "rocs_dca_cross_attn_noalloc": [P, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, P, P, c_int64,
+                            c_float, P, c_int64, P, c_int64, P],
     "rocs_broadcast_rows": [P, c_int64, P, c_int64, P, c_int64, P],
     "rocs_stack_workspace_size": [P, c_int32, c_int32],
     "rocs_stack_forward": [P, P, P, P, c_size_t, P],
@@ -298,6 +300,17 @@ def rocs_dca_cross_attn(batch_, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld
                                    ptr(k_r), ptr(v_r), ptr(k_c), ptr(v_c), ld_kv, float(scale), ptr(a_r), ld_ar,
                                    ptr(a_c), ld_ac, ptr(workspace), ws_bytes, stream)
     return _check(st) if check else st
+
+
+def rocs_dca_cross_attn_noalloc(batch_, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld_qc, k_r, v_r, k_c, v_c,
+                                ld_kv, scale, a_r, ld_ar, a_c, ld_ac, stream=None, check=True):
+    st = lib().rocs_dca_cross_attn_noalloc(_b(batch_), dtype, n_heads, head_dim, L, ptr(q_r), ld_qr, ptr(q_c), ld_qc,
+                                           ptr(k_r), ptr(v_r), ptr(k_c), ptr(v_c), ld_kv, float(scale), ptr(a_r),
+                                           ld_ar, ptr(a_c), ld_ac, stream)
+    return _check(st) if check else st
+
+
+ROCS_XATTN_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 def rocs_broadcast_rows(batch_, row_bytes, src, src_stride, dst, dst_stride, stream=None, check=True):

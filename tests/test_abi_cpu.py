@@ -262,3 +262,19 @@ def test_w8a16_argument_checks():
     assert call(s=None) == R.ROCS_ERR_INVALID_ARG and "w_scale" in R.last_error()
     assert call(act=5) == R.ROCS_ERR_INVALID_ARG
     assert call(M=0) == R.ROCS_OK  # empty: nothing launched
+
+
+def test_noalloc_cross_attention_rejects_batches_beyond_its_scratch():
+    # The plan of 1.5M candidates needs more than the 4 MiB static scratch:
+    # refused on the host, before anything is enqueued.
+    text = open(HEADER).read()
+    assert "#define ROCS_XATTN_NOALLOC_SCRATCH_BYTES (4 << 20)" in text
+    assert R.ROCS_XATTN_NOALLOC_SCRATCH_BYTES == 4 << 20
+    b = R.batch(2, 1_500_000, None, FAKE)
+    st = R.rocs_dca_cross_attn_noalloc(b, R.ROCS_BF16, 2, 64, 32, FAKE, 128, FAKE, 128, FAKE, FAKE, FAKE, FAKE, 512,
+                                       0.125, FAKE, 128, FAKE, 128, check=False)
+    assert st == R.ROCS_ERR_WORKSPACE
+    assert "static scratch" in R.last_error()
+    st = R.rocs_dca_cross_attn_noalloc(b, R.ROCS_F32, 2, 64, 32, FAKE, 128, FAKE, 128, FAKE, FAKE, FAKE, FAKE, 512,
+                                       0.125, FAKE, 128, FAKE, 128, check=False)
+    assert st == R.ROCS_ERR_DTYPE
