@@ -233,6 +233,27 @@ int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_hea
                         const void* v_r, const void* k_c, const void* v_c, int64_t ld_kv, float scale, void* a_r,
                         int64_t ld_ar, void* a_c, int64_t ld_ac, void* workspace, size_t ws_bytes, void* stream);
 
+/* Request-side cross-attention computed from the encoder output ([R] §2.2,
+ * grouped cross-attention of the request query group, one query row per
+ * request and head): a_r[b] = concat_h softmax(q_h K_h^T * scale) V_h with
+ * K = S W_K^T and V = S W_V^T over request b's L events S[b*L .. b*L+L-1].
+ * With a single query per request and head, the keys and values need not
+ * be projected: the call re-associates the products, scores
+ * (W_K,h^T q_h) . S_l and output W_V,h (sum_l p_h(l) S_l), exactly equal in
+ * real arithmetic (fp32 accumulation, one bf16 rounding of the output).
+ *   seq    [B_r * L, ld_s] bf16 (rows of request b at b*L)
+ *   wk_r, wv_r  [d, d] bf16, [out, in] (row stride d), d = 64 * n_heads
+ *   q_r    [B_r, ld_qr], a_r [B_r, ld_ar] bf16
+ *   scale  score scale (0 selects 1/sqrt(64))
+ * n_heads in {1, 2, 4, 8} and L <= 65536 (else ROCS_ERR_UNSUPPORTED); bf16 only.
+ * Workspace: rocs_dca_request_attn_workspace_size (fp32 q' and per-chunk
+ * partial sums).  The stack executor uses this path for the request query
+ * group and projects only the candidates' keys and values. */
+size_t rocs_dca_request_attn_workspace_size(int32_t B_r, int32_t n_heads, int32_t L);
+int rocs_dca_request_attn(rocs_dtype dtype, int32_t B_r, int32_t n_heads, int32_t L, const void* q_r, int64_t ld_qr,
+                          const void* seq, int64_t ld_s, const void* wk_r, const void* wv_r, float scale, void* a_r,
+                          int64_t ld_ar, void* workspace, size_t ws_bytes, void* stream);
+
 /* Variant of rocs_dca_cross_attn that allocates nothing and takes no
  * workspace, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -333,18 +333,25 @@ int layer_norm_rows(int rows, int width, void* x, int64_t ld, const void* g, con
   return ROCS_OK;
 }
 
+// Encoder output S_k (k = 0..n_enc) of encode_kv_launch: S_0 is the input
+// sequence, S_1.. live at the start of the encoder workspace.
+const void* encoder_output(const void* seq, void* workspace, int k, int rows, int d) {
+  if (k == 0) return seq;
+  return reinterpret_cast<char*>(workspace) + size_t(k - 1) * align_up(size_t(rows) * d * 2, 256);
+}
+
+// cand_only: project only the candidate keys and values, kv[j] = [K_C | V_C]
+// ([rows, 2d] per depth) for callers that compute the request side from S
+// itself (rocs_rqattn.hip); otherwise kv[j] = [K_R | V_R | K_C | V_C].
 int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t ffn, const void* seq, int32_t n_enc,
                      const rocs_enc_layer* enc, int32_t n_depths, const int32_t* depth_src, const rocs_kv_w* kvw,
-                     void* kv, void* workspace, hipStream_t s) {
+                     void* kv, void* workspace, hipStream_t s, bool cand_only = false) {
   if (B_r == 0) return ROCS_OK;
   const int rows = B_r * L;
   char* w = reinterpret_cast<char*>(workspace);
   std::vector<void*> S(n_enc + 1);
-  S[0] = const_cast<void*>(seq);
-  for (int k = 1; k <= n_enc; ++k) {
-    S[k] = w;
-    w += align_up(size_t(rows) * d * 2, 256);
-  }
+  for (int k = 0; k <= n_enc; ++k) S[k] = const_cast<void*>(encoder_output(seq, workspace, k, rows, d));
+  w += align_up(size_t(rows) * d * 2, 256) * size_t(n_enc);
   bf16* qkv = reinterpret_cast<bf16*>(w);
   w += align_up(size_t(rows) * 3 * d * 2, 256);
   bf16* att = reinterpret_cast<bf16*>(w);
@@ -383,23 +390,24 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
     ROCS_TRY(gemm_plain(hid, ffn, rows, d, ffn, e.w_2, e.b_2, 0, tmp, d, S[k + 1], d, s, "encoder ffn2"));
     ROCS_TRY(layer_norm_rows(rows, d, S[k + 1], d, e.ln2_g, e.ln2_b, s));
   }
+  const int nseg = cand_only ? 2 : 4;
   for (int j = 0; j < n_depths; ++j) {
     GemmArgs g{};
     g.M = rows;
-    g.N = 4 * d;
+    g.N = nseg * d;
     g.K = d;
     g.A = S[depth_src[j]];
     g.lda = d;
-    g.nseg = 4;
-    g.W[0] = kvw[j].wk_r;
-    g.W[1] = kvw[j].wv_r;
-    g.W[2] = kvw[j].wk_c;
-    g.W[3] = kvw[j].wv_c;
-    for (int q = 0; q < 4; ++q) g.seg_end[q] = (q + 1) * d;
+    g.nseg = nseg;
+    const void* ws4[4] = {kvw[j].wk_r, kvw[j].wv_r, kvw[j].wk_c, kvw[j].wv_c};
+    for (int q = 0; q < nseg; ++q) {
+      g.W[q] = ws4[4 - nseg + q];
+      g.seg_end[q] = (q + 1) * d;
+    }
     g.ldw = d;
-    g.n_split = 4 * d;
-    g.out0 = reinterpret_cast<bf16*>(kv) + size_t(j) * rows * 4 * d;
-    g.ld0 = 4 * d;
+    g.n_split = nseg * d;
+    g.out0 = reinterpret_cast<bf16*>(kv) + size_t(j) * rows * nseg * d;
+    g.ld0 = nseg * d;
     ROCS_HIP(launch_gemm(BF16, g, s), "K/V projection");
   }
   return ROCS_OK;
@@ -889,6 +897,49 @@ int rocs_dca_cross_attn_noalloc(const rocs_batch* batch, rocs_dtype dtype, int32
     ROCS_TRY(xattn_candidate_launch(B_r, B_c, p, n_heads, L, q_c, ld_qc, k_c, v_c, ld_kv, int64_t(L) * ld_kv, sl2,
                                     a_c, ld_ac, nullptr, s));
   }
+  return ok();
+}
+
+size_t rocs_dca_request_attn_workspace_size(int32_t B_r, int32_t n_heads, int32_t L) {
+  if (B_r < 0 || !rq_attn_supported(n_heads, L)) return 0;
+  return rq_attn_ws_bytes(B_r, L, n_heads);
+}
+
+int rocs_dca_request_attn(rocs_dtype dtype, int32_t B_r, int32_t n_heads, int32_t L, const void* q_r, int64_t ld_qr,
+                          const void* seq, int64_t ld_s, const void* wk_r, const void* wv_r, float scale, void* a_r,
+                          int64_t ld_ar, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "rocs_dca_request_attn";
+  ROCS_TRY(check_dtype(dtype, true, fn));
+  ROCS_TRY(check_nonneg(B_r, fn, "B_r"));
+  if (L <= 0) return fail(ROCS_ERR_INVALID_ARG, "%s: L must be > 0", fn);
+  if (!rq_attn_supported(n_heads, L))
+    return fail(ROCS_ERR_UNSUPPORTED, "%s: n_heads must be 1, 2, 4 or 8 and L at most 65536", fn);
+  if (B_r == 0) return ok();
+  const int64_t d = int64_t(n_heads) * 64;
+  ROCS_TRY(check_mat(q_r, ld_qr, d, 2, true, fn, "q_r"));
+  ROCS_TRY(check_mat(seq, ld_s, d, 2, true, fn, "seq"));
+  ROCS_TRY(check_mat(a_r, ld_ar, d, 2, true, fn, "a_r"));
+  ROCS_TRY(check_weight(wk_r, d, 2, fn, "wk_r"));
+  ROCS_TRY(check_weight(wv_r, d, 2, fn, "wv_r"));
+  const size_t need = rq_attn_ws_bytes(B_r, L, n_heads);
+  if (!workspace || ws_bytes < need) return fail(ROCS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+  ROCS_TRY(check_ptr(workspace, fn, "workspace"));
+  RqAttnArgs a{};
+  a.B_r = B_r;
+  a.H = n_heads;
+  a.L = L;
+  a.q = reinterpret_cast<const bf16*>(q_r);
+  a.ldq = ld_qr;
+  a.s = reinterpret_cast<const bf16*>(seq);
+  a.lds = ld_s;
+  a.wk = reinterpret_cast<const bf16*>(wk_r);
+  a.wv = reinterpret_cast<const bf16*>(wv_r);
+  a.ldw = d;
+  a.scale_log2 = scale_log2_of(scale);
+  a.o = reinterpret_cast<bf16*>(a_r);
+  a.ldo = ld_ar;
+  rq_attn_carve(a, workspace);
+  ROCS_HIP(launch_rq_attn(a, as_stream(stream)), fn);
   return ok();
 }
 

@@ -159,6 +159,30 @@ int attn_tile_rows();
 
 // Builds per-request query tiles (and, without offsets, a counting sort of
 // cand2req into a permutation).  ws layout is returned through the pointers.
+// Request-side cross-attention from the encoder output (rocs_rqattn.hip):
+// o[b, h*64 + e] = W_V,h (softmax_l(q'_h . S_l) S) with q'_h = W_K,h^T q_h,
+// one query per request; d = 64 H, H in {1, 2, 4, 8}; S rows 16-byte aligned.
+struct RqAttnArgs {
+  int B_r, H, L;
+  const bf16* q;
+  int64_t ldq;
+  const bf16* s;  // [B_r * L, lds], rows of request b at b*L
+  int64_t lds;
+  const bf16* wk;  // [d, d] ([out, in]), row stride ldw
+  const bf16* wv;
+  int64_t ldw;
+  float scale_log2;  // score scale times log2(e)
+  bf16* o;
+  int64_t ldo;
+  float* qf;       // workspace (rq_attn_carve)
+  float* part_u;
+  float* part_ml;
+};
+size_t rq_attn_ws_bytes(int B_r, int L, int H);
+void rq_attn_carve(RqAttnArgs& a, void* ws);
+bool rq_attn_supported(int H, int L);
+hipError_t launch_rq_attn(const RqAttnArgs& a, hipStream_t s);
+
 size_t attn_plan_ws_bytes(int B_r, int B_c);
 hipError_t launch_attn_plan(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, void* ws,
                             int32_t** tile_info, int32_t** n_tiles, int32_t** perm, int* max_tiles, hipStream_t s);

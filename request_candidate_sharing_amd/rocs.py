@@ -140,6 +140,9 @@ _SIGS = {
     "rocs_dca_encode_kv": [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, P, c_int32, P, c_int32, P, P, P, P,
                            c_size_t, P],
     "rocs_dca_cross_attn_workspace_size": [c_int32, c_int32, c_int32, c_int32],
+    "rocs_dca_request_attn_workspace_size": [c_int32, c_int32, c_int32],
+    "rocs_dca_request_attn": [c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, c_float, P, c_int64, P,
+                              c_size_t, P],
     "rocs_dca_cross_attn": [P, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, P, P, c_int64,
                             c_float, P, c_int64, P, c_int64, P, c_size_t, P],
     "rocs_dca_cross_attn_noalloc": [P, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P, P, P, c_int64,
@@ -161,6 +164,7 @@ _SIGS = {
 _RES = {
     "rocs_dca_encode_kv_workspace_size": c_size_t,
     "rocs_dca_cross_attn_workspace_size": c_size_t,
+    "rocs_dca_request_attn_workspace_size": c_size_t,
     "rocs_stack_workspace_size": c_size_t,
     "rocs_ugsep_workspace_size": c_size_t,
     "rocs_status_str": ctypes.c_char_p,
@@ -299,6 +303,17 @@ def rocs_dca_cross_attn(batch_, dtype, n_heads, head_dim, L, q_r, ld_qr, q_c, ld
     st = lib().rocs_dca_cross_attn(_b(batch_), dtype, n_heads, head_dim, L, ptr(q_r), ld_qr, ptr(q_c), ld_qc,
                                    ptr(k_r), ptr(v_r), ptr(k_c), ptr(v_c), ld_kv, float(scale), ptr(a_r), ld_ar,
                                    ptr(a_c), ld_ac, ptr(workspace), ws_bytes, stream)
+    return _check(st) if check else st
+
+
+def rocs_dca_request_attn_workspace_size(B_r, n_heads, L) -> int:
+    return int(lib().rocs_dca_request_attn_workspace_size(B_r, n_heads, L))
+
+
+def rocs_dca_request_attn(dtype, B_r, n_heads, L, q_r, ld_qr, seq, ld_s, wk_r, wv_r, scale, a_r, ld_ar, workspace,
+                          ws_bytes, stream=None, check=True):
+    st = lib().rocs_dca_request_attn(dtype, B_r, n_heads, L, ptr(q_r), ld_qr, ptr(seq), ld_s, ptr(wk_r), ptr(wv_r),
+                                     float(scale), ptr(a_r), ld_ar, ptr(workspace), ws_bytes, stream)
     return _check(st) if check else st
 
 

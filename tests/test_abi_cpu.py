@@ -278,3 +278,20 @@ def test_noalloc_cross_attention_rejects_batches_beyond_its_scratch():
     st = R.rocs_dca_cross_attn_noalloc(b, R.ROCS_F32, 2, 64, 32, FAKE, 128, FAKE, 128, FAKE, FAKE, FAKE, FAKE, 512,
                                        0.125, FAKE, 128, FAKE, 128, check=False)
     assert st == R.ROCS_ERR_DTYPE
+
+
+def test_request_attention_argument_checks():
+    ws = R.rocs_dca_request_attn_workspace_size(4, 8, 1024)
+    # fp32 q' (4 x 8 x 512) and per-64-event chunk partials (4 x 16 x 8 x 512 + maxima and sums)
+    assert ws >= 4 * 8 * 512 * 4 + 4 * 16 * 8 * 512 * 4
+    assert R.rocs_dca_request_attn_workspace_size(4, 3, 1024) == 0  # 3 heads: unsupported
+    call = lambda **kw: R.rocs_dca_request_attn(**{**dict(dtype=R.ROCS_BF16, B_r=4, n_heads=8, L=1024, q_r=FAKE,
+                                                            ld_qr=512, seq=FAKE, ld_s=512, wk_r=FAKE, wv_r=FAKE,
+                                                            scale=0.0, a_r=FAKE, ld_ar=512, workspace=FAKE,
+                                                            ws_bytes=ws), **kw}, check=False)
+    assert call(n_heads=3) == R.ROCS_ERR_UNSUPPORTED
+    assert call(dtype=R.ROCS_F32) == R.ROCS_ERR_DTYPE
+    assert call(ld_s=256) == R.ROCS_ERR_SHAPE
+    assert call(seq=FAKE + 8) == R.ROCS_ERR_ALIGN
+    assert call(ws_bytes=ws - 1) == R.ROCS_ERR_WORKSPACE
+    assert call(wk_r=None) == R.ROCS_ERR_INVALID_ARG

@@ -466,3 +466,28 @@ def test_token_lcb_parity(nr, nc, D, tr, tc):
     assert rel_err(to_np(yc), ref_c) <= TOL_BF16
     ref_r_req, _ = ops.token_lcb(np.concatenate([xr, np.zeros((B, nc, D))], 1), W, nr, tr)
     assert rel_err(to_np(yr), ref_r_req) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,L,H", [(3, 200, 2), (2, 1024, 8), (5, 64, 4), (4, 1, 1), (2, 130, 8)])
+def test_request_attention_from_encoder_output(B, L, H):
+    """rocs_dca_request_attn (request query group attending from S with the
+    products re-associated) against the oracle's attention over K = S W_K^T,
+    V = S W_V^T, projected explicitly in float64."""
+    R = _R()
+    rng = np.random.default_rng(L + 7 * H)
+    d = 64 * H
+    q = rand(rng, (B, d), True)
+    S_ = rand(rng, (B * L, d), True)
+    wk = rand(rng, (d, d), True, scale=d ** -0.5)
+    wv = rand(rng, (d, d), True, scale=d ** -0.5)
+    a = torch.full((B, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wsb = R.rocs_dca_request_attn_workspace_size(B, H, L)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    R.rocs_dca_request_attn(R.ROCS_BF16, B, H, L, dev(q, torch.bfloat16), d, dev(S_, torch.bfloat16), d,
+                            dev(wk, torch.bfloat16), dev(wv, torch.bfloat16), 0.0, a, d, ws, wsb, R.cur_stream())
+    torch.cuda.synchronize()
+    S64 = S_.astype(np.float64).reshape(B, L, d)
+    K = S64 @ wk.astype(np.float64).T
+    V = S64 @ wv.astype(np.float64).T
+    ref = ops.attention(q[:, None, :], K, V, H)[:, 0]
+    assert rel_err(to_np(a), ref) <= TOL_BF16
