@@ -293,7 +293,17 @@ int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* 
  * overwrite rows other tiles still read), with two element-wise
  * exceptions: a NORM may run in place (src view == dst view), and a
  * residual view may equal the output view.  Other overlaps are rejected
- * with ROCS_ERR_INVALID_ARG before anything is enqueued. */
+ * with ROCS_ERR_INVALID_ARG before anything is enqueued.
+ * Widths whose rows are not whole 16-byte chunks (e.g. 37 bf16 elements)
+ * are zero-padded in the workspace ([R] §2.4, the alignment fix of the
+ * decomposed dimensions): caller slots of such widths are staged through
+ * padded copies (any row stride >= width, element-aligned pointers), GLM
+ * weight blocks with such input widths are copied into padded rows once per
+ * call, and the columns after such an input view are zeroed, so every GEMM
+ * reads whole 16-byte chunks.  Column offsets of views stay multiples of 16
+ * bytes, and no view may cover the zero padding after a ragged GLM input
+ * (ROCS_ERR_ALIGN).  The standalone rocs_lcb_* calls read caller rows in
+ * 16-byte chunks and keep requiring them. */
 typedef enum rocs_exec_mode {
   ROCS_EXEC_SHARED = 0,         /* request work at B_r size, map resolved in-kernel */
   ROCS_EXEC_DENSE_BROADCAST = 1 /* comparator: request contributions and K/V copied to B_c rows first */

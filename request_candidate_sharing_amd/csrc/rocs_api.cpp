@@ -149,7 +149,7 @@ int lcb_request_check(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_xr
 int lcb_request_launch(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_xr, int32_t d_in_r, const void* w_rr,
                        const void* w_cr, const void* b_r, int32_t d_out_r, int32_t d_out_c, int act,
                        const void* res_r, int64_t ld_resr, void* y_r, int64_t ld_yr, float* z, int64_t ld_z,
-                       hipStream_t s) {
+                       hipStream_t s, int64_t ldw = 0) {
   if (B_r == 0 || d_out_r + d_out_c == 0) return ROCS_OK;
   GemmArgs g{};
   g.M = B_r;
@@ -168,7 +168,7 @@ int lcb_request_launch(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_x
     g.W[0] = d_out_r > 0 ? w_rr : w_cr;
     g.seg_end[0] = g.N;
   }
-  g.ldw = d_in_r;
+  g.ldw = ldw > 0 ? ldw : d_in_r;  // padded weight rows (stack executor) or contiguous ones
   g.n_split = d_out_r;
   g.out0 = y_r;
   g.ld0 = ld_yr;
@@ -233,10 +233,12 @@ GemmArgs lcb_candidate_args(int B_c, int B_r, const int32_t* zmap, const void* x
 
 int lcb_candidate_launch(int B_c, int B_r, const int32_t* zmap, rocs_dtype dt, const void* x_c, int64_t ld_xc,
                          int32_t d_in_c, const void* w_cc, const void* b_c, int32_t d_out_c, int act, const float* z,
-                         int64_t ld_z, const void* res_c, int64_t ld_resc, void* y_c, int64_t ld_yc, hipStream_t s) {
+                         int64_t ld_z, const void* res_c, int64_t ld_resc, void* y_c, int64_t ld_yc, hipStream_t s,
+                         int64_t ldw = 0) {
   if (B_c == 0 || d_out_c == 0) return ROCS_OK;
-  const GemmArgs g = lcb_candidate_args(B_c, B_r, zmap, x_c, ld_xc, d_in_c, w_cc, b_c, d_out_c, act, z, ld_z, res_c,
-                                        ld_resc, y_c, ld_yc);
+  GemmArgs g = lcb_candidate_args(B_c, B_r, zmap, x_c, ld_xc, d_in_c, w_cc, b_c, d_out_c, act, z, ld_z, res_c,
+                                  ld_resc, y_c, ld_yc);
+  if (ldw > 0) g.ldw = ldw;
   ROCS_HIP(launch_gemm(DType(dt), g, s), "rocs_lcb_candidate");
   return ROCS_OK;
 }

@@ -254,6 +254,9 @@ struct MlpArgs {
 bool mlp_block_supported(int d_in, int hidden, int d_out);
 hipError_t launch_mlp_block(const MlpArgs& a, hipStream_t s);
 
+// dst[r][c] = src[r][c] (c < w), 0 (w <= c < wpad); src NULL: zero [w, wpad) only
+hipError_t launch_pad_rows(int64_t rows, int w, int wpad, int es, const void* src, int64_t lds, void* dst,
+                           int64_t ldd, hipStream_t s);
 hipError_t launch_validate_batch(int B_r, int B_c, const int32_t* offsets, const int32_t* cand2req, int32_t* flag,
                                  hipStream_t s);
 

@@ -232,6 +232,24 @@ __global__ __launch_bounds__(256) void rowdot_kernel(DotArgs a) {
   }
 }
 
+// ----------------------------------------------------------------- zero padding
+// dst[r][c] = src[r][c] for c < w and 0 for w <= c < wpad (rows of es-byte
+// elements, any strides).  With src == NULL only [w, wpad) is written (the
+// zero tail after a view of width w).  Element by element: for weights,
+// staged inputs and outputs of widths that break 16-byte rows.
+template <typename E>
+__global__ __launch_bounds__(256) void pad_rows_kernel(int64_t rows, int w, int wpad, const E* __restrict__ src,
+                                                       int64_t lds, E* __restrict__ dst, int64_t ldd) {
+  const int c0 = src ? 0 : w;
+  const int span = wpad - c0;
+  const int64_t total = rows * span;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total; e += int64_t(gridDim.x) * 256) {
+    const int64_t r = e / span;
+    const int c = c0 + int(e - r * span);
+    dst[r * ldd + c] = c < w ? src[r * lds + c] : E(0);
+  }
+}
+
 // ----------------------------------------------------------------- explicit broadcast
 // dst[i] = src[map[i]] byte for byte; 16 bytes per thread.
 __global__ __launch_bounds__(256) void bcast_kernel(int64_t rows, const int32_t* map, int map_rows, int64_t chunks,
@@ -306,6 +324,20 @@ hipError_t launch_broadcast_rows(int rows, const int32_t* map, int map_rows, int
   hipLaunchKernelGGL(bcast_kernel, dim3(grid), dim3(256), 0, s, all_rows, map, map_rows, chunks,
                      reinterpret_cast<const uint4*>(src), src_stride / 16, reinterpret_cast<uint4*>(dst),
                      dst_stride / 16, inner);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(int64_t rows, int w, int wpad, int es, const void* src, int64_t lds, void* dst,
+                           int64_t ldd, hipStream_t s) {
+  const int64_t total = rows * (wpad - (src ? 0 : w));
+  if (rows <= 0 || total <= 0) return hipSuccess;
+  const int64_t g = std::min<int64_t>((total + 255) / 256, 8192);
+  if (es == 2)
+    hipLaunchKernelGGL(pad_rows_kernel<uint16_t>, dim3(unsigned(g)), dim3(256), 0, s, rows, w, wpad,
+                       static_cast<const uint16_t*>(src), lds, static_cast<uint16_t*>(dst), ldd);
+  else
+    hipLaunchKernelGGL(pad_rows_kernel<uint32_t>, dim3(unsigned(g)), dim3(256), 0, s, rows, w, wpad,
+                       static_cast<const uint32_t*>(src), lds, static_cast<uint32_t*>(dst), ldd);
   return hipGetLastError();
 }
 

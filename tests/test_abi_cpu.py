@@ -295,3 +295,20 @@ def test_request_attention_argument_checks():
     assert call(seq=FAKE + 8) == R.ROCS_ERR_ALIGN
     assert call(ws_bytes=ws - 1) == R.ROCS_ERR_WORKSPACE
     assert call(wk_r=None) == R.ROCS_ERR_INVALID_ARG
+
+
+def test_stack_accepts_ragged_widths():
+    # widths of 37 / 45 / 33 bf16 elements (rows that are not whole 16-byte
+    # chunks) are zero-padded inside the workspace: staged caller rows and
+    # padded weight blocks make the workspace larger than the aligned case
+    ragged = _glm_mlp_desc(d=37, H=33, n_blocks=1)
+    aligned = _glm_mlp_desc(d=40, H=40, n_blocks=1)
+    a = R.rocs_stack_workspace_size(ragged, 4, 100)
+    b = R.rocs_stack_workspace_size(aligned, 4, 100)
+    assert a > 0, R.last_error()
+    assert a > b
+    # the standalone GLM linear reads caller rows in 16-byte chunks and keeps
+    # rejecting them
+    st = R.rocs_lcb_request(R.ROCS_BF16, 4, FAKE, 40, 37, FAKE, FAKE, None, 33, 33, 0, None, 0, FAKE, 40, FAKE, 40,
+                            check=False)
+    assert st == R.ROCS_ERR_ALIGN

@@ -117,6 +117,32 @@ def test_fused_mlp_block_matches_unfused_layers(k):
         assert np.array_equal(a["y_c"], b["y_c"])
 
 
+RAGGED = [(1, dict(d_r=37, d_c=45, hidden=33)),
+          (2, dict(d_r=37, d_c=45, hidden=33, hidden_r=41)),
+          (2, dict(d_r=36, d_c=44, hidden=36))]
+
+
+@pytest.mark.parametrize("k,widths", RAGGED)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_ragged_widths_are_zero_padded(k, widths, mode):
+    # [R] §2.4 alignment fix: widths whose rows are not whole 16-byte chunks
+    # (37, 45, 33 bf16 or fp32 elements).  The stack stages the caller's rows
+    # through padded copies, pads the weight blocks per call and zeroes the
+    # tails of its own slots; results match the oracle like aligned widths.
+    cfg = S.small_config(k).with_(**widths)
+    inp = S.make_inputs(cfg)
+    _, got = _stack(inp, mode=mode)
+    _compare(cfg, got, oracle.oracle_forward(inp))
+
+
+def test_ragged_widths_shared_matches_dense_bitwise():
+    cfg = S.small_config(2).with_(d_r=37, d_c=45, hidden=33)
+    inp = S.make_inputs(cfg)
+    _, a = _stack(inp, mode=0)
+    _, b = _stack(inp, mode=1)
+    assert np.array_equal(a["y_c"], b["y_c"]) and np.array_equal(a["y_r"], b["y_r"])
+
+
 @pytest.mark.parametrize("r", [2, 3])
 def test_request_side_scaled_stack_parity(r):
     # Request-side scaling r ([R] §2.3): the GLM MLP stack with request
