@@ -182,6 +182,8 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
+ROOFLINE_KERNEL = ("gemm_bf16_big_kernel<256, 256, 2, 4, 2> via rocs_lcb_candidate (interaction-layer MLP1 of the "
+                   "ranking stack, layers 2-4: B_c x 1024 -> B_c x 2048, ReLU, Z[m_i] epilogue)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_ranking_stack.json")
 # sources the candidate GEMM is compiled from (the counters are void once any of them changes)
 GEMM_SRCS = [os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", f)
@@ -567,6 +569,8 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
     ap.add_argument("--workload", type=int, default=5,
                     help="5 (default) is the benchmark line; 1-4 time another workload's stack (profiling aid)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the dominant kernel's timing (the ranking stack's MLP1 candidate GEMM), for counters")
     ap.add_argument("--rrr", action="store_true",
                     help="study: request-side scaling r x candidates per request N on the GLM MLP stack shapes")
     ap.add_argument("--rrr-r", default="1,2,4")
@@ -610,6 +614,15 @@ def main():
         return other_workload(args)
 
     cfg = S.config(5)
+    if args.roofline_only:
+        b = S.make_batch(S.make_inputs(cfg.with_(L=1, n_enc=0, n_int=0, head=False))["counts"])
+        c2r = torch.as_tensor(b["cand2req"], device="cuda")
+        offs = torch.as_tensor(b["offsets"], device="cuda")
+        B_r, B_c = cfg.B, int(b["offsets"][-1])
+        rf = candidate_gemm_roofline(R.batch(B_r, B_c, offs, c2r), B_r, B_c, 2 * cfg.d_seq, cfg.hidden,
+                                     ROOFLINE_KERNEL, args.roofline_reps)
+        print(json.dumps({"roofline_only": rf}), flush=True)
+        return
     inp = S.make_inputs(cfg)
     B_r, B_c = cfg.B, int(len(inp["cand2req"]))
     log(f"bench: {cfg.name()} B_r={B_r} B_c={B_c}")
@@ -669,10 +682,7 @@ def main():
         log(f"bench: step latency p50 {out['step_latency']['p50_ms']:.3f} ms, "
             f"p99 {out['step_latency']['p99_ms']:.3f} ms")
     K, N = 2 * cfg.d_seq, cfg.hidden
-    out["roofline"] = candidate_gemm_roofline(
-        shared.batch, B_r, B_c, K, N,
-        "gemm_bf16_big_kernel<256, 256, 2, 4, 2> via rocs_lcb_candidate (interaction-layer MLP1 of the ranking "
-        "stack, layers 2-4: B_c x 1024 -> B_c x 2048, ReLU, Z[m_i] epilogue)", args.roofline_reps)
+    out["roofline"] = candidate_gemm_roofline(shared.batch, B_r, B_c, K, N, ROOFLINE_KERNEL, args.roofline_reps)
     log(f"bench: candidate GEMM {out['roofline']['avg_launch_us']:.1f} us/launch, "
         f"{out['roofline']['achieved']:.1f} {out['roofline']['unit']} ({out['roofline']['frac']:.3f} of peak)")
     del shared

@@ -1,6 +1,7 @@
 // Group-local norms, the scalar score head, the explicit broadcast used by
 // the dense-broadcast comparator, and batch validation.
 #include <algorithm>
+#include <type_traits>
 
 #include "rocs_device.h"
 
@@ -10,30 +11,24 @@ namespace {
 
 // ----------------------------------------------------------------- group-local norm
 // [R] §2.1, Figure 2(b): statistics inside one group's slice of a row.  One
-// wave per row; the row (x + res) stays in registers between the statistics
-// and the normalisation, so each element is read once and written once.
-// LayerNorm: two-pass mean / biased variance in fp32; RMSNorm: mean square.
-// One launch can normalize two independent row groups (the request and the
-// candidate part of a stack layer): workgroups [0, nblk_a) take group pa,
-// the rest group pb.
+// wave per row, RPW consecutive rows per wave: every 16-byte load of the
+// wave's rows (and residuals) is issued before any is used, so a wave keeps
+// RPW x CH loads per lane in flight.  A row stays in registers between the
+// statistics and the normalisation, so each element is read once and
+// written once.  LayerNorm: two-pass mean / biased variance in fp32;
+// RMSNorm: mean square.  One launch can normalize two independent row groups
+// (the request and the candidate part of a stack layer): workgroups
+// [0, nblk_a) take group pa, the rest group pb.
 // RES: some group of the launch adds a residual (the other may not).
-template <typename T, int CH, bool RES>
+template <typename T, int CH, bool RES, int RPW>
 __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int nblk_a) {
   constexpr int VEC = 16 / sizeof(T);
   const bool second = int(blockIdx.x) >= nblk_a;
   const NormArgs a = second ? pb : pa;
   const int lane = threadIdx.x & 63;
-  const int row = (second ? int(blockIdx.x) - nblk_a : int(blockIdx.x)) * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
-  const T* r = a.res ? reinterpret_cast<const T*>(a.res) + int64_t(row) * (a.ldres ? a.ldres : a.ldx) : nullptr;
-  // the fused head's gathered request dot, requested before the row
-  float hz = 0.f;
-  if (a.head_w && a.head_z) {
-    const int m = a.head_zmap ? a.head_zmap[row] : row;
-    hz = ((unsigned)m < (unsigned)a.head_zrows) ? a.head_z[m] : nan_f();
-  }
-  // and the head weights of this lane's chunks
+  const int row0 = ((second ? int(blockIdx.x) - nblk_a : int(blockIdx.x)) * 4 + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= a.rows) return;
+  // head weights of this lane's chunks (the same for every row)
   const T* hw = reinterpret_cast<const T*>(a.head_w);
   uint4 hwv[CH];
 #pragma unroll
@@ -41,149 +36,183 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs pa, NormArgs pb, int
     const int e0 = (c * 64 + lane) * VEC;
     hwv[c] = (hw && e0 + VEC <= a.width) ? *reinterpret_cast<const uint4*>(hw + e0) : make_uint4(0, 0, 0, 0);
   }
-  // every chunk's loads are issued before any is used, so a wave keeps all
-  // of its row's 16-byte loads in flight at once
-  // (one uniform branch around all of them: a lane whose vector is not
-  // whole in the row loads the row's last whole vector instead and ignores
-  // it; rows narrower than one vector take the element path below)
-  // with RES the residual is loaded unconditionally (from x when this group
-  // has none) and added by a select, so no branch separates the loads
+  // every chunk's loads of every row, issued before any is used (one uniform
+  // branch around all of them: a lane whose vector is not whole in the row
+  // loads the row's last whole vector instead and ignores it; rows narrower
+  // than one vector take the element path below).  With RES the residual is
+  // loaded unconditionally (from x when this group has none) and added by a
+  // select, so no branch separates the loads.
   const bool has_r = RES && a.res != nullptr;
-  const T* rp = (RES && r) ? r : x;
-  uint4 xq[CH], rq[CH];
+  const int64_t ldr = a.ldres ? a.ldres : a.ldx;
   const int last_vec = (a.width / VEC - 1) * VEC;
+  uint4 xq[RPW][CH], rq[RPW][CH];
+  float hz[RPW];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) xq[c] = rq[c] = make_uint4(0, 0, 0, 0);
-  if (a.width >= VEC) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int e0 = (c * 64 + lane) * VEC;
-      const int el = e0 + VEC <= a.width ? e0 : last_vec;
-      xq[c] = *reinterpret_cast<const uint4*>(x + el);
-      if (RES) rq[c] = *reinterpret_cast<const uint4*>(rp + el);
+  for (int j = 0; j < RPW; ++j) {
+    const int row = min(row0 + j, a.rows - 1);  // rows past the end repeat the last one and store nothing
+    hz[j] = 0.f;
+    if (a.head_w && a.head_z) {
+      const int m = a.head_zmap ? a.head_zmap[row] : row;
+      hz[j] = ((unsigned)m < (unsigned)a.head_zrows) ? a.head_z[m] : nan_f();
     }
-  }
-  // Each loaded value is consumed here, in chunk order, after the last load
-  // was issued: the compiler may not move a load down next to its use (with
-  // one chunk there is nothing to order).
-  if constexpr (CH > 1) {
+    const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
+    const T* rp = has_r ? reinterpret_cast<const T*>(a.res) + int64_t(row) * ldr : x;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      asm volatile("" ::"v"(xq[c].x), "v"(xq[c].y), "v"(xq[c].z), "v"(xq[c].w) : "memory");
-      if (RES) asm volatile("" ::"v"(rq[c].x), "v"(rq[c].y), "v"(rq[c].z), "v"(rq[c].w) : "memory");
-    }
-  }
-  float v[CH][VEC];
-  float s = 0.f;
+    for (int c = 0; c < CH; ++c) xq[j][c] = rq[j][c] = make_uint4(0, 0, 0, 0);
+    if (a.width >= VEC) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e0 = (c * 64 + lane) * VEC;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) v[c][j] = 0.f;
-    if (e0 + VEC <= a.width) {
-      const T* t = reinterpret_cast<const T*>(&xq[c]);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) v[c][j] = to_f(t[j]);
-      if (RES) {
-        const T* tr = reinterpret_cast<const T*>(&rq[c]);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) v[c][j] = has_r ? v[c][j] + to_f(tr[j]) : v[c][j];
+      for (int c = 0; c < CH; ++c) {
+        const int e0 = (c * 64 + lane) * VEC;
+        const int el = e0 + VEC <= a.width ? e0 : last_vec;
+        xq[j][c] = *reinterpret_cast<const uint4*>(x + el);
+        if (RES) rq[j][c] = *reinterpret_cast<const uint4*>(rp + el);
       }
-    } else {
-      for (int j = 0; j < VEC; ++j)
-        if (e0 + j < a.width) v[c][j] = to_f(x[e0 + j]) + (r ? to_f(r[e0 + j]) : 0.f);
     }
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) s += (a.kind == 0) ? v[c][j] : v[c][j] * v[c][j];
   }
-  const float inv_w = 1.0f / float(a.width);
-  float mean = 0.f, scale;
-  if (a.kind == 0) {
-    mean = wave_sum(s) * inv_w;
-    float q = 0.f;
+  // Each loaded value is consumed here, in order, after the last load was
+  // issued: the compiler may not move a load down next to its use.
+  if constexpr (CH * RPW > 1) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int e0 = (c * 64 + lane) * VEC;
+    for (int j = 0; j < RPW; ++j)
 #pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        if (e0 + j < a.width) {
-          const float d = v[c][j] - mean;
-          q += d * d;
-        }
-    }
-    scale = 1.0f / sqrtf(wave_sum(q) * inv_w + a.eps);
-  } else {
-    scale = 1.0f / sqrtf(wave_sum(s) * inv_w + a.eps);
+      for (int c = 0; c < CH; ++c) {
+        asm volatile("" ::"v"(xq[j][c].x), "v"(xq[j][c].y), "v"(xq[j][c].z), "v"(xq[j][c].w) : "memory");
+        if (RES) asm volatile("" ::"v"(rq[j][c].x), "v"(rq[j][c].y), "v"(rq[j][c].z), "v"(rq[j][c].w) : "memory");
+      }
   }
   const T* g = reinterpret_cast<const T*>(a.gamma);
   const T* b = reinterpret_cast<const T*>(a.beta);
-  T* y = reinterpret_cast<T*>(a.y) + int64_t(row) * a.ldy;
-  float hs = 0.f;  // fused head: the same chunks and order as rowdot_kernel
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e0 = (c * 64 + lane) * VEC;
-    if (e0 >= a.width) continue;
-    // affine parameters of this chunk in 16-byte loads (gamma and beta are
-    // 16-byte aligned); the ragged last chunk reads them element by element
-    T gv[VEC], bv[VEC];
-    if (e0 + VEC <= a.width) {
-      if (g) *reinterpret_cast<uint4*>(gv) = *reinterpret_cast<const uint4*>(g + e0);
-      if (b) *reinterpret_cast<uint4*>(bv) = *reinterpret_cast<const uint4*>(b + e0);
+  for (int j = 0; j < RPW; ++j) {
+    const int row = row0 + j;
+    if (row >= a.rows) continue;  // uniform across the wave
+    const T* x = reinterpret_cast<const T*>(a.x) + int64_t(row) * a.ldx;
+    const T* r = a.res ? reinterpret_cast<const T*>(a.res) + int64_t(row) * ldr : nullptr;
+    float v[CH][VEC];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e0 = (c * 64 + lane) * VEC;
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) v[c][k] = 0.f;
+      if (e0 + VEC <= a.width) {
+        const T* t = reinterpret_cast<const T*>(&xq[j][c]);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) v[c][k] = to_f(t[k]);
+        if (RES) {
+          const T* tr = reinterpret_cast<const T*>(&rq[j][c]);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) v[c][k] = has_r ? v[c][k] + to_f(tr[k]) : v[c][k];
+        }
+      } else {
+        for (int k = 0; k < VEC; ++k)
+          if (e0 + k < a.width) v[c][k] = to_f(x[e0 + k]) + (r ? to_f(r[e0 + k]) : 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) s += (a.kind == 0) ? v[c][k] : v[c][k] * v[c][k];
+    }
+    const float inv_w = 1.0f / float(a.width);
+    float mean = 0.f, scale;
+    if (a.kind == 0) {
+      mean = wave_sum(s) * inv_w;
+      float q = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int e0 = (c * 64 + lane) * VEC;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k)
+          if (e0 + k < a.width) {
+            const float dd = v[c][k] - mean;
+            q += dd * dd;
+          }
+      }
+      scale = 1.0f / sqrtf(wave_sum(q) * inv_w + a.eps);
     } else {
+      scale = 1.0f / sqrtf(wave_sum(s) * inv_w + a.eps);
+    }
+    T* y = reinterpret_cast<T*>(a.y) + int64_t(row) * a.ldy;
+    float hs = 0.f;  // fused head: the same chunks and order as rowdot_kernel
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const int e = min(e0 + j, a.width - 1);
-        if (g) gv[j] = g[e];
-        if (b) bv[j] = b[e];
+    for (int c = 0; c < CH; ++c) {
+      const int e0 = (c * 64 + lane) * VEC;
+      if (e0 >= a.width) continue;
+      // affine parameters of this chunk in 16-byte loads (gamma and beta are
+      // 16-byte aligned); the ragged last chunk reads them element by element
+      T gv[VEC], bv[VEC];
+      if (e0 + VEC <= a.width) {
+        if (g) *reinterpret_cast<uint4*>(gv) = *reinterpret_cast<const uint4*>(g + e0);
+        if (b) *reinterpret_cast<uint4*>(bv) = *reinterpret_cast<const uint4*>(b + e0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const int e = min(e0 + k, a.width - 1);
+          if (g) gv[k] = g[e];
+          if (b) bv[k] = b[e];
+        }
+      }
+      T out[VEC];
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        float t = (v[c][k] - mean) * scale;
+        if (g) t *= to_f(gv[k]);
+        if (b) t += to_f(bv[k]);
+        if (a.act == 1) t = fmaxf(t, 0.f);
+        out[k] = from_f<T>(t);
+      }
+      if (e0 + VEC <= a.width) {
+        *reinterpret_cast<uint4*>(y + e0) = *reinterpret_cast<const uint4*>(out);
+        if (hw) {
+          const T* tw = reinterpret_cast<const T*>(&hwv[c]);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) hs = fmaf(to_f(out[k]), to_f(tw[k]), hs);
+        }
+      } else {
+        for (int k = 0; k < VEC; ++k)
+          if (e0 + k < a.width) y[e0 + k] = out[k];
+        if (hw)
+          for (int k = 0; k < VEC && e0 + k < a.width; ++k) hs = fmaf(to_f(out[k]), to_f(hw[e0 + k]), hs);
       }
     }
-    T out[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      float t = (v[c][j] - mean) * scale;
-      if (g) t *= to_f(gv[j]);
-      if (b) t += to_f(bv[j]);
-      if (a.act == 1) t = fmaxf(t, 0.f);
-      out[j] = from_f<T>(t);
-    }
-    if (e0 + VEC <= a.width) {
-      *reinterpret_cast<uint4*>(y + e0) = *reinterpret_cast<const uint4*>(out);
-      if (hw) {
-        const T* tw = reinterpret_cast<const T*>(&hwv[c]);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) hs = fmaf(to_f(out[j]), to_f(tw[j]), hs);
+    if (hw) {
+      hs = wave_sum(hs);
+      if (lane == 0) {
+        if (a.head_z) hs = hs + hz[j];  // NaN for a map entry out of range
+        hs += a.head_bias;
+        if (a.head_bias_dev) hs += to_f(reinterpret_cast<const T*>(a.head_bias_dev)[0]);
+        a.head_out[row] = hs;
       }
-    } else {
-      for (int j = 0; j < VEC; ++j)
-        if (e0 + j < a.width) y[e0 + j] = out[j];
-      if (hw)
-        for (int j = 0; j < VEC && e0 + j < a.width; ++j) hs = fmaf(to_f(out[j]), to_f(hw[e0 + j]), hs);
-    }
-  }
-  if (hw) {
-    hs = wave_sum(hs);
-    if (lane == 0) {
-      if (a.head_z) hs = hs + hz;  // NaN for a map entry out of range
-      hs += a.head_bias;
-      if (a.head_bias_dev) hs += to_f(reinterpret_cast<const T*>(a.head_bias_dev)[0]);
-      a.head_out[row] = hs;
     }
   }
 }
 
+// Rows per wave.  One: measured on the GLM MLP stack (512-wide rows, 74k of
+// them) four rows per wave with all their loads in flight took 44 us against
+// 36 us for one row per wave (more registers per wave, fewer waves in flight),
+// and 12 vs 5 us for 256 rows.
+template <int CH>
+constexpr int norm_rpw() { return 1; }
+
 template <typename T, bool RES>
-hipError_t norm_launch(int ch, dim3 grid, const NormArgs& a, const NormArgs& b, int na, hipStream_t s) {
+hipError_t norm_launch(int ch, const NormArgs& a, const NormArgs& b, hipStream_t s) {
   const dim3 block(256);
+  auto go = [&](auto chc) -> hipError_t {
+    constexpr int CH = decltype(chc)::value;
+    constexpr int RPW = norm_rpw<CH>();
+    const int na = (a.rows + 4 * RPW - 1) / (4 * RPW);
+    const dim3 grid(na + (b.rows + 4 * RPW - 1) / (4 * RPW));
+    if (grid.x == 0) return hipSuccess;
+    hipLaunchKernelGGL((norm_kernel<T, CH, RES, RPW>), grid, block, 0, s, a, b, na);
+    return hipGetLastError();
+  };
   switch (ch <= 1 ? 1 : ch <= 2 ? 2 : ch <= 3 ? 3 : ch <= 4 ? 4 : ch <= 8 ? 8 : ch <= 16 ? 16 : 0) {
-    case 1: hipLaunchKernelGGL((norm_kernel<T, 1, RES>), grid, block, 0, s, a, b, na); break;
-    case 2: hipLaunchKernelGGL((norm_kernel<T, 2, RES>), grid, block, 0, s, a, b, na); break;
-    case 3: hipLaunchKernelGGL((norm_kernel<T, 3, RES>), grid, block, 0, s, a, b, na); break;
-    case 4: hipLaunchKernelGGL((norm_kernel<T, 4, RES>), grid, block, 0, s, a, b, na); break;
-    case 8: hipLaunchKernelGGL((norm_kernel<T, 8, RES>), grid, block, 0, s, a, b, na); break;
-    case 16: hipLaunchKernelGGL((norm_kernel<T, 16, RES>), grid, block, 0, s, a, b, na); break;
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 3: return go(std::integral_constant<int, 3>{});
+    case 4: return go(std::integral_constant<int, 4>{});
+    case 8: return go(std::integral_constant<int, 8>{});
+    case 16: return go(std::integral_constant<int, 16>{});
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <typename T>
@@ -191,10 +220,7 @@ hipError_t norm_dispatch(const NormArgs& a, const NormArgs& b, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   const int per = 64 * VEC;
   const int ch = std::max((a.width + per - 1) / per, (b.width + per - 1) / per);
-  const int na = (a.rows + 3) / 4;
-  const dim3 grid(na + (b.rows + 3) / 4);
-  if (grid.x == 0) return hipSuccess;
-  return (a.res || b.res) ? norm_launch<T, true>(ch, grid, a, b, na, s) : norm_launch<T, false>(ch, grid, a, b, na, s);
+  return (a.res || b.res) ? norm_launch<T, true>(ch, a, b, s) : norm_launch<T, false>(ch, a, b, s);
 }
 
 // ----------------------------------------------------------------- row dot (score head)
