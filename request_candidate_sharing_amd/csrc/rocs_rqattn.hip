@@ -8,15 +8,13 @@
 //   score_h(l) = q_h . (W_K,h S_l) = (W_K,h^T q_h) . S_l = q'_h . S_l
 //   A_h        = sum_l p_h(l) W_V,h S_l = W_V,h (sum_l p_h(l) S_l) = W_V,h u_h
 // with W_K,h, W_V,h the 64 rows of head h ([out, in] weights).  Three
-// launches, fp32 throughout (S and the weights are bf16):
+// launches, fp32 except S and the weights (bf16) and q' as an MFMA operand:
 //   rq_fold     q'_h = scale log2(e) W_K,h^T q_h          per (request, head)
-//   rq_attend   64 events per workgroup: scores of every head, the chunk's
-//               maximum m_h, p = 2^(s - m_h), l_h = sum p, u_h = sum p S_l
+//   rq_attend   64 events per workgroup: scores of every head (MFMA, q' in
+//               bf16), the chunk's maximum m_h, p = 2^(s - m_h), l_h = sum p,
+//               u_h = sum p S_l
 //   rq_combine  chunks merged per (request, head) in a fixed order,
 //               A_h = W_V,h (u_h / l_h), rounded once to bf16
-// Each lane of rq_attend owns H consecutive features of the d = 64 H wide
-// rows, so an event row is one coalesced load per wave and stays in
-// registers between its scores and its contribution to u.
 #include "rocs_device.h"
 
 namespace rocs {
@@ -145,53 +143,71 @@ __global__ __launch_bounds__(256) void rq_fold_kernel(RqAttnArgs a) {
     a.qf[(int64_t(b) * a.H + h) * d + i] = (((part[0][i] + part[1][i]) + part[2][i]) + part[3][i]) * a.scale_log2;
 }
 
+// Scores of a wave's 16 events for every head on v_mfma_f32_16x16x32_bf16:
+// the event rows are the first operand (lane l supplies row l % 16, eight K
+// elements at 8 (l / 16) of each 32-wide K step), q' rounded to bf16 the
+// second (column l % 16 = head; heads past H are zero), so lane l ends with
+// the scores of events 4 (l / 16) + j (j < 4) for head l % 16.  The
+// contributions p S_l to u then run on the VALU with a lane owning H
+// consecutive features (the rows are read again, from L2).
 template <int H>
 __global__ __launch_bounds__(256) void rq_attend_kernel(RqAttnArgs a) {
   constexpr int D = 64 * H;
+  constexpr int KB = D / 32;  // 32-wide K steps
   using Frag = typename RowFrag<H>::T;
   const int nch = (a.L + RQ_CHUNK - 1) / RQ_CHUNK;
   const int b = blockIdx.x / nch, ch = blockIdx.x - (blockIdx.x / nch) * nch;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kg = lane >> 4;
   __shared__ float sc[RQ_CHUNK][H];
   __shared__ float mx[H];
   __shared__ float ured[H][D];
   __shared__ float lred[4][H];
 
-  // this wave's events, one H-wide slice of each row per lane
-  Frag rows[RQ_WROWS];
   const int r0 = ch * RQ_CHUNK + wave * RQ_WROWS;
-  const bf16* sb = a.s + (int64_t(b) * a.L) * a.lds + lane * H;
+  const bf16* sb = a.s + (int64_t(b) * a.L) * a.lds;
+  // MFMA operands: this lane's event row and q' row, all K steps requested up front
+  uint4 sf[KB];
+  {
+    const int r = r0 + r16;
+    const bf16* rp = sb + int64_t(r < a.L ? r : 0) * a.lds + kg * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      sf[kb] = r < a.L ? *reinterpret_cast<const uint4*>(rp + kb * 32) : make_uint4(0, 0, 0, 0);
+  }
+  bf16x8 qf[KB];
+  {
+    const float* qp = a.qf + (int64_t(b) * H + (r16 < H ? r16 : 0)) * D + kg * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const float4 lo = *reinterpret_cast<const float4*>(qp + kb * 32);
+      const float4 hi = *reinterpret_cast<const float4*>(qp + kb * 32 + 4);
+      const bool on = r16 < H;
+      qf[kb] = bf16x8{to_bf(on ? lo.x : 0.f), to_bf(on ? lo.y : 0.f), to_bf(on ? lo.z : 0.f), to_bf(on ? lo.w : 0.f),
+                      to_bf(on ? hi.x : 0.f), to_bf(on ? hi.y : 0.f), to_bf(on ? hi.z : 0.f), to_bf(on ? hi.w : 0.f)};
+    }
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sf[kb]), qf[kb], acc, 0, 0, 0);
+  if (r16 < H) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = wave * RQ_WROWS + 4 * kg + j;
+      sc[rl][r16] = (ch * RQ_CHUNK + rl < a.L) ? acc[j] : -INFINITY;
+    }
+  }
+  // the rows again, one H-wide slice per lane, for the contributions to u
+  Frag rows[RQ_WROWS];
 #pragma unroll
   for (int j = 0; j < RQ_WROWS; ++j) {
     const int r = r0 + j;
-    rows[j] = r < a.L ? *reinterpret_cast<const Frag*>(sb + int64_t(r) * a.lds) : Frag{};
-  }
-  float qv[H][H];  // [head][element]
-  const float* qp = a.qf + int64_t(b) * H * D + lane * H;
-#pragma unroll
-  for (int h = 0; h < H; ++h)
-#pragma unroll
-    for (int e = 0; e < H; ++e) qv[h][e] = qp[h * D + e];
-
-  // scores (log2 units: q' carries scale * log2(e))
-  const int hsel = head_of_lane<H>(lane);
-  const bool writer = (lane & ((64 / H) - 1)) == 0;
-#pragma unroll
-  for (int j = 0; j < RQ_WROWS; ++j) {
-    float x[H];
-    unpack_row<H>(rows[j], x);
-    float part[H];
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < H; ++e) acc = fmaf(x[e], qv[h][e], acc);
-      part[h] = acc;
-    }
-    const float s = transpose_reduce<H, false>(part);
-    if (writer) sc[wave * RQ_WROWS + j][hsel] = (r0 + j < a.L) ? s : -INFINITY;
+    rows[j] = r < a.L ? *reinterpret_cast<const Frag*>(sb + int64_t(r) * a.lds + lane * H) : Frag{};
   }
   __syncthreads();
+  const int hsel = head_of_lane<H>(lane);
+  const bool writer = (lane & ((64 / H) - 1)) == 0;
   if (wave == 0) {
     float v[H];
 #pragma unroll
@@ -222,7 +238,8 @@ __global__ __launch_bounds__(256) void rq_attend_kernel(RqAttnArgs a) {
       for (int e = 0; e < H; ++e) u[h][e] = fmaf(p, x[e], u[h][e]);
     }
   }
-  // waves combine in a fixed order: ((u3 + u2) + u1) + u0
+  // waves combine in a fixed order: ((u3 + u2) + u1) + u0.  (A two-level
+  // tree through a lane-contiguous layout measured slower: 27 vs 22 us.)
   if (lane == 0)
 #pragma unroll
     for (int h = 0; h < H; ++h) lred[wave][h] = l[h];
@@ -264,9 +281,13 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(RqAttnArgs a) {
   const int nch = (a.L + RQ_CHUNK - 1) / RQ_CHUNK;
   __shared__ float us[D];
   __shared__ float wc[1024];
+  __shared__ float lc[1024];
   __shared__ float stats[2];
   const float* ml = a.part_ml + 2 * (int64_t(b) * nch * H + h);
-  for (int c = threadIdx.x; c < nch; c += 256) wc[c] = ml[2 * c * H];
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    wc[c] = ml[2 * c * H];
+    lc[c] = ml[2 * c * H + 1];
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     float M = -INFINITY;
@@ -279,7 +300,7 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(RqAttnArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) {
     float lsum = 0.f;
-    for (int c = 0; c < nch; ++c) lsum = fmaf(wc[c], ml[2 * c * H + 1], lsum);
+    for (int c = 0; c < nch; ++c) lsum = fmaf(wc[c], lc[c], lsum);
     stats[1] = 1.f / lsum;
   }
   __syncthreads();
