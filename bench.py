@@ -456,6 +456,25 @@ def ugsep_study(args):
         out.update(dense_ms_per_step=t_de / args.steps * 1e3, speedup_vs_dense=t_de / t_sh,
                    saved_fraction=1.0 - t_sh / t_de, flop_saved_fraction=1.0 - F / Fd,
                    dense_mfma_util_pct=100.0 * Fd / (t_de / args.steps) / PEAK_BF16)
+    # the U side's FFN on 8-bit weights (ROCS_UGSEP_SHARED_W8A16): whole
+    # step, and the U side alone (a batch with no candidates), bf16 vs W8A16
+    quant = S.make_ugsep_w8a16(inp)
+    w8 = DeviceUgsep(inp, mode=R.ROCS_UGSEP_SHARED_W8A16, quant=quant)
+    t_w8, _ = time_steps(w8.run, args.steps, args.warmup)
+    del w8
+    out.update(w8a16_ms_per_step=t_w8 / args.steps * 1e3, w8a16_candidates_per_s=B_c * args.steps / t_w8)
+    # (three copies of the weights in rotation, 315 MB or more of U weights,
+    # so the 256 MB MALL cannot serve them from one call to the next)
+    inp0 = S.make_ugsep_inputs(cfg, counts=[0] * cfg.B)
+    reps = 21 * args.steps
+    for mode, key, q in ((R.ROCS_UGSEP_SHARED, "u_side_bf16_us", None),
+                         (R.ROCS_UGSEP_SHARED_W8A16, "u_side_w8a16_us", quant)):
+        us = [DeviceUgsep(inp0, mode=mode, quant=q) for _ in range(3)]
+        it = iter(range(1 << 30))
+        t_u, _ = time_steps(lambda: us[next(it) % 3].run(), reps, args.warmup)
+        del us
+        out[key] = t_u / reps * 1e6
+    out["u_side_change_pct"] = 100.0 * (out["u_side_w8a16_us"] / out["u_side_bf16_us"] - 1.0)
     if not args.no_cpu:
         from oracle import ugsep as U
 
@@ -483,8 +502,10 @@ def w8a16_study(args):
 
     page = {(16, 1280, 2560): -50.2, (16, 1280, 640): -40.0, (8, 1280, 2560): -46.8, (8, 1280, 640): -55.0}
     st = R.cur_stream()
-    # the page's shapes, then two larger ones where the weight stream dominates
-    for (M, K, N) in S.W8A16_SHAPES + [(16, 4096, 4096), (16, 8192, 8192)]:
+    # the page's shapes, then larger ones where the weight stream dominates, and
+    # more activation rows
+    for (M, K, N) in S.W8A16_SHAPES + [(16, 4096, 4096), (16, 8192, 8192), (32, 1280, 2560), (64, 1280, 2560),
+                                       (32, 4096, 4096)]:
         d = S.make_w8a16_inputs(M, K, N)
         x = torch.as_tensor(d["x"], device="cuda").to(torch.bfloat16)
         y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")

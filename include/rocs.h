@@ -416,6 +416,15 @@ typedef struct rocs_ugsep_layer {
   const void* b2;          /* [T, dim] (nullable = 0) */
   const void* ln2_gamma;   /* [dim] */
   const void* ln2_beta;    /* [dim] */
+  /* ROCS_UGSEP_SHARED_W8A16 only (else ignored): the U tokens' FFN weights as
+   * 8-bit E4M3 codes with one fp32 scale per output channel, in the encoding
+   * rocs_w8a16_linear reads; w1 and w2 are then read for the G tokens only.
+   * Token t < n_u computes with w1_scale[t, h] * e4m3(w1_q[t, h, :]) and
+   * w2_scale[t, d] * e4m3(w2_q[t, d, :]). */
+  const uint8_t* w1_q;     /* [n_u, hidden, dim] codes */
+  const float* w1_scale;   /* [n_u, hidden] */
+  const uint8_t* w2_q;     /* [n_u, dim, hidden] codes */
+  const float* w2_scale;   /* [n_u, dim] */
 } rocs_ugsep_layer;
 
 typedef struct rocs_ugsep_desc {
@@ -426,8 +435,15 @@ typedef struct rocs_ugsep_desc {
 
 typedef enum rocs_ugsep_mode {
   ROCS_UGSEP_SHARED = 0, /* U side once per request */
-  ROCS_UGSEP_DENSE = 1   /* comparator: U tokens copied to every candidate and
+  ROCS_UGSEP_DENSE = 1,  /* comparator: U tokens copied to every candidate and
                             recomputed per candidate; y_u is not written */
+  ROCS_UGSEP_SHARED_W8A16 = 2 /* shared, with the U side's FFN on 8-bit weights
+                            ([U] §3 stage 4 and the W8A16 configuration: the
+                            per-request U side is a small-batch, weight-bound
+                            layer).  bf16 only; needs the layers' w1_q/w2_q
+                            codes and scales, num_requests <= 64, dim and hidden
+                            multiples of 128; ROCS_ERR_UNSUPPORTED otherwise.  The G side is as
+                            in ROCS_UGSEP_SHARED. */
 } rocs_ugsep_mode;
 
 /* u_comp [B_r, n_g * dim] fp32 (ld_uc) = P x_u along the token axis (the
@@ -465,7 +481,7 @@ int rocs_ugsep_forward(const rocs_ugsep_desc* desc, const rocs_batch* batch, roc
  * w_scale: [N] fp32, one scale per output channel.  x: [M, K] bf16 (ld_x),
  * bias: [N] bf16 (nullable), y: [M, N] bf16 (ld_y).  Products accumulate in
  * fp32; the scale, bias and ReLU are applied once at the end.
- * Supported: 1 <= M <= 64, N a multiple of 32, K a positive multiple of 128
+ * Supported: 1 <= M <= 64, N a multiple of 16, K a positive multiple of 128
  * (ROCS_ERR_UNSUPPORTED otherwise); x, w_q, y 16-byte aligned with 16-byte
  * row strides (ROCS_ERR_ALIGN).  M == 0 or N == 0 is a no-op. */
 int rocs_w8a16_linear(int32_t M, int32_t N, int32_t K, const void* x, int64_t ld_x, const uint8_t* w_q, int64_t ld_w,

@@ -139,6 +139,28 @@ def tokenmixer(X: np.ndarray, layers: Sequence[Dict[str, Any]], n_u: int, eps: f
     return X
 
 
+def with_u_w8a16(layers: Sequence[Dict[str, Any]], quant: Sequence[Dict[str, Any]], n_u: int) -> list:
+    """Layers whose U tokens' FFN weights are the dequantized 8-bit weights
+    ([U] §3 framework tree stage 4 and the W8A16 configuration; readings
+    W1-W2 of the W8A16 oracle): token t < n_u uses
+    W1_t = w1_scale[t] * fp8(w1_q[t]) and W2_t = w2_scale[t] * fp8(w2_q[t]);
+    the G tokens keep their weights.  The layer itself is unchanged, so the
+    result is the TokenMixer of ``tokenmixer`` with these weights."""
+    from . import w8a16
+
+    out = []
+    for p, q in zip(layers, quant):
+        r = dict(p)
+        w1 = np.array(p["w1"], dtype=F64)
+        w2 = np.array(p["w2"], dtype=F64)
+        for t in range(n_u):
+            w1[t] = w8a16.dequantize(q["w1_q"][t], q["w1_scale"][t])
+            w2[t] = w8a16.dequantize(q["w2_q"][t], q["w2_scale"][t])
+        r["w1"], r["w2"] = w1, w2
+        out.append(r)
+    return out
+
+
 def ugsep_forward(inputs: Dict[str, Any], candidates=None, requests=None) -> Dict[str, np.ndarray]:
     """Stack outputs for the listed candidates and requests (default: all).
 

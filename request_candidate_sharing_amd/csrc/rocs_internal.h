@@ -310,7 +310,14 @@ struct W8Args {
   int act;
   bf16* y;
   int64_t ldy;
+  const bf16* res;  // optional residual added after the activation (ld = ldres)
+  int64_t ldres;
+  // optional batch of `batch` GEMMs of this shape (grid.y): GEMM i reads x, wq,
+  // scale, bias, res and writes y at i times these element strides
+  int batch;
+  int64_t sx, sw, sscale, sbias, sres, sy;
 };
+bool w8a16_supported(int M, int N, int K);
 hipError_t launch_w8a16(const W8Args& a, hipStream_t s);
 hipError_t launch_mixup_norm(DType dt, const MixupArgs& a, hipStream_t s);
 

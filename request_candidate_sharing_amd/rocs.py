@@ -100,6 +100,7 @@ class rocs_ugsep_layer(ctypes.Structure):
     _fields_ = [
         ("comp", c_void_p), ("ln1_gamma", c_void_p), ("ln1_beta", c_void_p), ("w1", c_void_p), ("b1", c_void_p),
         ("w2", c_void_p), ("b2", c_void_p), ("ln2_gamma", c_void_p), ("ln2_beta", c_void_p),
+        ("w1_q", c_void_p), ("w1_scale", c_void_p), ("w2_q", c_void_p), ("w2_scale", c_void_p),
     ]
 
 
@@ -112,6 +113,7 @@ class rocs_ugsep_desc(ctypes.Structure):
 
 ROCS_UGSEP_SHARED = 0
 ROCS_UGSEP_DENSE = 1
+ROCS_UGSEP_SHARED_W8A16 = 2
 
 
 class RocsError(RuntimeError):
@@ -362,7 +364,8 @@ def ugsep_desc(n_u, n_g, dim, hidden, eps, layers) -> rocs_ugsep_desc:
     arr = (rocs_ugsep_layer * len(layers))()
     for i, L in enumerate(layers):
         arr[i] = rocs_ugsep_layer(*(ptr(L.get(k)) for k in ("comp", "ln1_g", "ln1_b", "w1", "b1", "w2", "b2",
-                                                            "ln2_g", "ln2_b")))
+                                                            "ln2_g", "ln2_b", "w1_q", "w1_scale", "w2_q",
+                                                            "w2_scale")))
     d = rocs_ugsep_desc(n_u, n_g, dim, hidden, len(layers), float(eps), arr)
     d._keep = (arr, layers)
     return d

@@ -249,7 +249,9 @@ class DeviceUgsep:
     §3) on a GPU: token rows, per-layer weights, descriptor, workspace and
     outputs.  Marshalling only; rocs_ugsep_forward does the work."""
 
-    def __init__(self, inputs: Dict[str, Any], device="cuda", mode: int = R.ROCS_UGSEP_SHARED):
+    def __init__(self, inputs: Dict[str, Any], device="cuda", mode: int = R.ROCS_UGSEP_SHARED, quant=None):
+        """``quant``: per-layer dicts of the U tokens' 8-bit weights (w1_q,
+        w1_scale, w2_q, w2_scale) for ROCS_UGSEP_SHARED_W8A16."""
         torch = _torch()
         self.inputs, self.mode = inputs, mode
         cfg = inputs["cfg"]
@@ -273,6 +275,11 @@ class DeviceUgsep:
             d = {k: t(p[k]) for k in ("ln1_g", "ln1_b", "w1", "b1", "w2", "b2", "ln2_g", "ln2_b")}
             d["comp"] = None if p["comp"] is None else t(p["comp"], torch.float32)
             layers.append(d)
+        for d, q in zip(layers, quant or ()):
+            for k in ("w1_q", "w2_q"):
+                d[k] = torch.as_tensor(np.ascontiguousarray(q[k], dtype=np.uint8), device=device)
+            for k in ("w1_scale", "w2_scale"):
+                d[k] = t(q[k], torch.float32)
         self.desc = R.ugsep_desc(n_u, n_g, D, H, inputs["eps"], layers)
         self.batch = R.batch(self.B_r, self.B_c, self.offs, self.c2r)
         self.ws_bytes = R.rocs_ugsep_workspace_size(self.desc, self.dtype, self.B_r, self.B_c, mode)

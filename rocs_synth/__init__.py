@@ -411,6 +411,32 @@ def make_ugsep_inputs(cfg: UgsepConfig, seed: int = 211, counts=None) -> Dict[st
     return out
 
 
+def make_ugsep_w8a16(inputs: Dict[str, Any], seed: int = 223) -> list:
+    """8-bit weights of the U tokens' FFNs for the UG-Sep W8A16 mode, one
+    dict per layer: w1_q [n_u, hidden, dim] and w2_q [n_u, dim, hidden] codes
+    drawn uniformly from the finite E4M3 codes (every byte except 0x7F and
+    0xFF), and per-output-channel scales w1_scale [n_u, hidden], w2_scale
+    [n_u, dim] ~ U(0.5, 1.5) / (100 sqrt(fan_in)) (the finite codes' values
+    have an RMS of about 100, so the weights have about the bf16 weights'
+    spread).  Draw order: layers in order (w1_q, w1_scale, w2_q, w2_scale)."""
+    rng = np.random.default_rng(seed)
+    n_u, D, H = int(inputs["n_u"]), int(inputs["dim"]), int(inputs["hidden"])
+
+    def codes(shape):
+        c = rng.integers(0, 254, shape).astype(np.uint8)
+        return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)  # skip 0x7F; 0xFF is never drawn
+
+    out = []
+    for _ in inputs["layers"]:
+        q: Dict[str, Any] = {}
+        q["w1_q"] = codes((n_u, H, D))
+        q["w1_scale"] = (rng.uniform(0.5, 1.5, (n_u, H)) / (100.0 * math.sqrt(D))).astype(np.float32)
+        q["w2_q"] = codes((n_u, D, H))
+        q["w2_scale"] = (rng.uniform(0.5, 1.5, (n_u, D)) / (100.0 * math.sqrt(H))).astype(np.float32)
+        out.append(q)
+    return out
+
+
 def shuffle_ugsep_candidates(inputs: Dict[str, Any], seed: int = 7) -> Dict[str, Any]:
     """Same UG-Sep batch with candidate rows in a random global order (offsets None)."""
     rng = np.random.default_rng(seed)

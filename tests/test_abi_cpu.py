@@ -238,6 +238,27 @@ def test_ugsep_forward_argument_checks():
     assert fwd(_ug_desc(dim=4096, n_u=8, n_g=8)) == R.ROCS_ERR_UNSUPPORTED  # wider than one wave's registers hold
 
 
+def test_ugsep_w8a16_mode_argument_checks():
+    W8 = R.ROCS_UGSEP_SHARED_W8A16
+    q = dict(w1_q=FAKE, w1_scale=FAKE, w2_q=FAKE, w2_scale=FAKE)
+    assert R.rocs_ugsep_workspace_size(_ug_desc(**q), R.ROCS_BF16, 32, 10056, W8) == \
+        R.rocs_ugsep_workspace_size(_ug_desc(**q), R.ROCS_BF16, 32, 10056, R.ROCS_UGSEP_SHARED)
+
+    def fwd(desc, B_r=2, dtype=R.ROCS_BF16, ld=8 * 1280):
+        b = R.batch(B_r, 6, None, FAKE)
+        return R.rocs_ugsep_forward(desc, b, dtype, W8, FAKE, ld, FAKE, ld, FAKE, ld, FAKE, ld, FAKE, 1 << 40,
+                                    check=False)
+
+    assert fwd(_ug_desc(**q), dtype=R.ROCS_F32, ld=8 * 1280) == R.ROCS_ERR_UNSUPPORTED  # 8-bit weights, bf16 only
+    assert fwd(_ug_desc()) == R.ROCS_ERR_INVALID_ARG  # no codes
+    assert fwd(_ug_desc(**dict(q, w2_scale=None))) == R.ROCS_ERR_INVALID_ARG
+    assert "w2_scale" in R.last_error()
+    assert fwd(_ug_desc(**dict(q, w1_q=FAKE + 8))) == R.ROCS_ERR_ALIGN
+    assert fwd(_ug_desc(**q), B_r=65) == R.ROCS_ERR_UNSUPPORTED  # more activation rows than the kernel takes
+    assert fwd(_ug_desc(n_u=4, n_g=4, dim=960, hidden=1920, **q), ld=8 * 960) == R.ROCS_ERR_UNSUPPORTED  # 960 % 128
+    assert fwd(_ug_desc(n_u=2, n_g=2, dim=256, hidden=400, **q), B_r=20, ld=4 * 256) == R.ROCS_ERR_UNSUPPORTED  # 400 % 128
+
+
 def test_ugsep_step_argument_checks():
     b = R.batch(2, 6, None, FAKE)
     st = R.rocs_ugsep_mixup_norm(b, R.ROCS_BF16, 2, 2, 64, 1e-5, FAKE, 128, FAKE, 128, None, 0, None, FAKE, FAKE,
@@ -255,6 +276,7 @@ def test_w8a16_argument_checks():
 
     assert call(M=65) == R.ROCS_ERR_UNSUPPORTED
     assert call(N=2550) == R.ROCS_ERR_UNSUPPORTED
+    assert call(M=40, N=2536, ldy=2536) == R.ROCS_ERR_UNSUPPORTED  # N a multiple of 16
     assert call(K=1200, ldx=1200, ldw=1200) == R.ROCS_ERR_UNSUPPORTED
     assert call(x=FAKE + 2) == R.ROCS_ERR_ALIGN
     assert call(ldw=1272) == R.ROCS_ERR_SHAPE

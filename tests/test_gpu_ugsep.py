@@ -45,16 +45,21 @@ def _rows(a, ld, tdt):
     return st
 
 
-def _layers(inp, tdt):
+def _layers(inp, tdt, quant=None):
     out = []
     for p in inp["layers"]:
         d = {k: dev(p[k], tdt) for k in ("ln1_g", "ln1_b", "w1", "b1", "w2", "b2", "ln2_g", "ln2_b")}
         d["comp"] = None if p["comp"] is None else torch.as_tensor(p["comp"], dtype=torch.float32, device="cuda")
         out.append(d)
+    for d, q in zip(out, quant or ()):
+        for k in ("w1_q", "w2_q"):
+            d[k] = torch.as_tensor(np.ascontiguousarray(q[k]), dtype=torch.uint8, device="cuda")
+        for k in ("w1_scale", "w2_scale"):
+            d[k] = torch.as_tensor(q[k], dtype=torch.float32, device="cuda")
     return out
 
 
-def run_forward(inp, dtype, mode=0, pad=0):
+def run_forward(inp, dtype, mode=0, pad=0, quant=None):
     """Runs rocs_ugsep_forward; returns (y_u [B_r, n_u, D], y_g [B_c, n_g, D]) as numpy."""
     R = _R()
     tdt = _tdt(dtype)
@@ -67,7 +72,7 @@ def run_forward(inp, dtype, mode=0, pad=0):
     yg = torch.full((max(B_c, 1), max(ldg, 8)), float("nan"), dtype=tdt, device="cuda")
     c2r = torch.as_tensor(inp["cand2req"], dtype=torch.int32, device="cuda")
     offs = None if inp.get("offsets") is None else torch.as_tensor(inp["offsets"], dtype=torch.int32, device="cuda")
-    desc = R.ugsep_desc(n_u, n_g, D, H, inp["eps"], _layers(inp, tdt))
+    desc = R.ugsep_desc(n_u, n_g, D, H, inp["eps"], _layers(inp, tdt, quant))
     need = R.rocs_ugsep_workspace_size(desc, _rdt(R, dtype), B_r, B_c, mode)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     R.rocs_ugsep_forward(desc, R.batch(B_r, B_c, offs, c2r), _rdt(R, dtype), mode, xu, max(ldu, 8), xg, max(ldg, 8),
@@ -252,3 +257,49 @@ def test_full_size_dense_comparator_sampled():
     cand = np.unique(np.concatenate([[0, B_c - 1], np.random.default_rng(2).integers(0, B_c, 14)]))
     ref = U.ugsep_forward(inp, candidates=cand, requests=[])
     assert rel_err(y_g[cand], ref["y_g"]) <= tol("bf16")
+
+
+# ------------------------------------------------------------------ U side on 8-bit weights
+
+W8_CASES = [  # requests (activation rows of the U side's GEMMs), shuffled candidates
+    (5, False),   # up to 16 rows: 16 output channels per workgroup
+    (24, True),   # 17..32 rows: one 32-row tile
+    (40, False),  # 33..64 rows: two tiles, ragged
+    (64, False),  # the largest request count the mode takes
+]
+
+
+@pytest.mark.parametrize("B,shuffled", W8_CASES)
+def test_w8a16_u_side_matches_oracle_on_dequantized_weights(B, shuffled):
+    """ROCS_UGSEP_SHARED_W8A16 against the oracle TokenMixer whose U tokens'
+    FFN weights are the dequantized codes (G outputs read U tokens through
+    the Mixup, so both sides are checked)."""
+    cfg = S.UgsepConfig("w8", B, ("uniform", 0, 6), 2, 2, 256, 384, 2, True, "bf16")
+    inp = S.make_ugsep_inputs(cfg, seed=400 + B)
+    if shuffled:
+        inp = S.shuffle_ugsep_candidates(inp, seed=5)
+    quant = S.make_ugsep_w8a16(inp, seed=410 + B)
+    R = _R()
+    y_u, y_g = run_forward(inp, "bf16", R.ROCS_UGSEP_SHARED_W8A16, quant=quant)
+    ref = U.ugsep_forward(dict(inp, layers=U.with_u_w8a16(inp["layers"], quant, inp["n_u"])))
+    assert rel_err(y_u, ref["y_u"]) <= tol("bf16")
+    assert rel_err(y_g, ref["y_g"]) <= tol("bf16")
+    # the 8-bit weights are the ones used: the bf16 U weights give other outputs
+    plain = U.ugsep_forward(inp, requests=[0], candidates=[])
+    assert rel_err(y_u[:1], plain["y_u"]) > 10 * tol("bf16")
+
+
+def test_w8a16_u_side_full_size_sampled():
+    """The benchmarked TokenMixer (8 U + 8 G tokens, width 1280, FFN 2560,
+    2 layers, 32 requests) with the U side on 8-bit weights, sampled rows."""
+    inp = S.make_ugsep_inputs(S.ugsep_config("tokenmixer"))
+    quant = S.make_ugsep_w8a16(inp)
+    y_u, y_g = run_forward(inp, "bf16", _R().ROCS_UGSEP_SHARED_W8A16, quant=quant)
+    assert np.isfinite(y_g).all() and np.isfinite(y_u).all()
+    B_c = len(inp["cand2req"])
+    cand = np.unique(np.concatenate([[0, B_c - 1], np.random.default_rng(3).integers(0, B_c, 10)]))
+    req = np.array([0, 13, 31])
+    ref = U.ugsep_forward(dict(inp, layers=U.with_u_w8a16(inp["layers"], quant, inp["n_u"])), candidates=cand,
+                          requests=req)
+    assert rel_err(y_g[cand], ref["y_g"]) <= tol("bf16")
+    assert rel_err(y_u[req], ref["y_u"]) <= tol("bf16")

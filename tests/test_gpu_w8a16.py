@@ -46,8 +46,9 @@ def run(x, codes, scale, bias, act, pad=0):
     return ys[:, :N].float().cpu().numpy()
 
 
-def test_every_finite_code_decodes_exactly():
-    M, N, K = 32, 256, 128
+@pytest.mark.parametrize("M", [16, 32, 64])  # one, two and four activation row tiles
+def test_every_finite_code_decodes_exactly(M):
+    N, K = 256, 128
     x = np.zeros((M, K), np.float32)
     x[np.arange(M), np.arange(M)] = 1.0  # row m picks weight column m
     codes = np.zeros((N, K), np.uint8)
@@ -81,6 +82,16 @@ CASES = [  # M, K, N, bias, act, padded
     (33, 1024, 128, True, 1, 0),
     (64, 128, 64, True, 0, 16),  # largest M, smallest K, two output tiles, padded
     (32, 2048, 32, False, 0, 0),  # one activation tile exactly, two blocks per wave
+    (3, 256, 48, True, 1, 0),  # N a multiple of 16 only
+    (40, 256, 48, True, 0, 0),  # N a multiple of 16 only, three row tiles
+    (17, 512, 64, True, 0, 8),  # first row count with two row tiles
+    (16, 8192, 16, True, 0, 0),  # one workgroup, eight blocks per wave through the double buffer
+    (40, 4096, 64, False, 1, 0),  # three row tiles, four blocks per wave
+    (5, 1152, 80, True, 0, 0),  # nine blocks over eight waves
+    (16, 1024, 5120, True, 0, 0),  # 320 channel tiles: the last launch with 16 channels per workgroup
+    (16, 1024, 5152, True, 1, 8),  # 322 tiles: 32 channels and four waves per workgroup
+    (48, 512, 5376, True, 0, 0),  # 32 channels per workgroup, three row tiles
+    (64, 256, 5632, False, 1, 0),  # 32 channels per workgroup, four row tiles
 ]
 
 

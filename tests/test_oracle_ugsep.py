@@ -193,3 +193,38 @@ def test_forward_subsets_match_the_whole_batch():
     part = U.ugsep_forward(inp, candidates=cand, requests=req)
     np.testing.assert_array_equal(part["y_g"], full["y_g"][cand])
     np.testing.assert_array_equal(part["y_u"], full["y_u"][req])
+
+
+# ------------------------------------------------------------------ U side on 8-bit weights
+
+def test_u_w8a16_substitution_with_hand_decoded_codes():
+    """with_u_w8a16 against weights written out by hand from the E4M3
+    format: 0x38 = +1 (exponent field 7 = bias, mantissa 0), 0xB8 = -1,
+    0x40 = +2, 0x30 = +0.5, 0x01 = 2^-9 (smallest subnormal).  The U tokens
+    take scale x those values; the G tokens keep their weights."""
+    cfg = S.UgsepConfig("w8pin", 2, ("fixed", 2), 2, 2, 8, 6, 1, True, "f32")
+    inp = S.make_ugsep_inputs(cfg, seed=31)
+    rng = _rng(5)
+    table = {0x38: 1.0, 0xB8: -1.0, 0x40: 2.0, 0x30: 0.5, 0x01: 2.0 ** -9}
+    keys = np.array(list(table), dtype=np.uint8)
+    q1 = keys[rng.integers(0, len(keys), (2, 6, 8))]
+    q2 = keys[rng.integers(0, len(keys), (2, 8, 6))]
+    s1, s2 = rng.uniform(0.5, 1.5, (2, 6)), rng.uniform(0.5, 1.5, (2, 8))
+    quant = [dict(w1_q=q1, w1_scale=s1, w2_q=q2, w2_scale=s2)]
+    lay = U.with_u_w8a16(inp["layers"], quant, 2)[0]
+    hand1 = np.vectorize(table.get)(q1) * s1[:, :, None]
+    hand2 = np.vectorize(table.get)(q2) * s2[:, :, None]
+    np.testing.assert_array_equal(lay["w1"][:2], hand1)
+    np.testing.assert_array_equal(lay["w2"][:2], hand2)
+    np.testing.assert_array_equal(lay["w1"][2:], inp["layers"][0]["w1"][2:])
+    np.testing.assert_array_equal(lay["w2"][2:], inp["layers"][0]["w2"][2:])
+    for k in ("b1", "b2", "ln1_g", "ln2_b", "comp"):
+        np.testing.assert_array_equal(lay[k], inp["layers"][0][k])
+    # and the layer with them is the layer with the hand weights
+    hand = dict(inp["layers"][0])
+    hand["w1"] = np.concatenate([hand1, inp["layers"][0]["w1"][2:]])
+    hand["w2"] = np.concatenate([hand2, inp["layers"][0]["w2"][2:]])
+    a = U.ugsep_forward(dict(inp, layers=[lay]))
+    b = U.ugsep_forward(dict(inp, layers=[hand]))
+    np.testing.assert_array_equal(a["y_g"], b["y_g"])
+    np.testing.assert_array_equal(a["y_u"], b["y_u"])
