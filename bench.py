@@ -349,6 +349,10 @@ def other_workload(args):
     del st
     out = {"workload": args.workload, "name": cfg.name(), "B_r": B_r, "B_c": B_c,
            "ms_per_step": t_sh / args.steps * 1e3, "candidates_per_s": B_c * args.steps / t_sh}
+    ser = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    t_se, _ = time_steps(ser.run, args.steps, args.warmup)
+    del ser
+    out["serial_schedule_ms_per_step"] = t_se / args.steps * 1e3
     if not args.no_dense:
         de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
         t_de, _ = time_steps(de.run, args.steps, args.warmup)
@@ -563,6 +567,10 @@ def glm_stack_line(args):
            "B_r": B_r, "B_c": B_c, "ms_per_step": sh * 1e3, "candidates_per_s": B_c / sh,
            "mfma_util_pct": 100.0 * F / sh / PEAK_BF16, "hbm_util_pct": 100.0 * Bts / sh / PEAK_HBM}
     del st
+    ser = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    t_se, _ = time_steps(ser.run, args.steps, args.warmup)
+    del ser
+    out["serial_schedule_ms_per_step"] = t_se / args.steps * 1e3
     if not args.no_dense:
         de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
         t_de, _ = time_steps(de.run, args.steps, args.warmup)
@@ -689,6 +697,12 @@ def main():
         "alg_flops_per_step": F,
         "alg_bytes_per_step": Bts,
     }
+    # the same launches with every one on the caller's stream (no request lane)
+    ser = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    t_se, _ = time_steps(ser.run, args.steps, args.warmup)
+    del ser
+    out["serial_schedule"] = {"ms_per_step": t_se / args.steps * 1e3, "two_lane_saving_ms": t_se / args.steps * 1e3 - ms}
+    log(f"bench: serial schedule {t_se / args.steps * 1e3:.3f} ms/step")
     if dense_out is not None:
         out["dense_broadcast"] = dense_out
         out["speedup_vs_dense_broadcast"] = dense_out["ms_per_step"] / ms

@@ -305,9 +305,26 @@ int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* 
  * (ROCS_ERR_ALIGN).  The standalone rocs_lcb_* calls read caller rows in
  * 16-byte chunks and keep requiring them. */
 typedef enum rocs_exec_mode {
-  ROCS_EXEC_SHARED = 0,         /* request work at B_r size, map resolved in-kernel */
-  ROCS_EXEC_DENSE_BROADCAST = 1 /* comparator: request contributions and K/V copied to B_c rows first */
+  ROCS_EXEC_SHARED = 0,          /* request work at B_r size, map resolved in-kernel */
+  ROCS_EXEC_DENSE_BROADCAST = 1, /* comparator: request contributions and K/V copied to B_c rows first */
+  ROCS_EXEC_SHARED_SERIAL = 2    /* as ROCS_EXEC_SHARED, every launch on the caller's stream */
 } rocs_exec_mode;
+/* Schedule of ROCS_EXEC_SHARED with both row groups present and a DCA
+ * descriptor ([R] §2.4: the request and candidate tiles share the GPU, the
+ * dependency on the request contribution is a completion signal instead of a
+ * kernel boundary; stacks without DCA, whose request side is the GLM request
+ * GEMMs alone, run as ROCS_EXEC_SHARED_SERIAL): the request rows' work runs
+ * on an internal stream of the device (created once
+ * per device at default priority, kept until the process ends) and the
+ * candidate rows' work on the caller's stream.  A candidate launch that reads
+ * a request result (Z, the request dots of the head, the keys and values of
+ * the encoder) first waits for an event recorded after its producer; the
+ * internal stream starts after an event recorded on the caller's stream at
+ * the call, and the caller's stream waits for the internal one at the end, so
+ * to the caller the call is ordered on its stream as one unit (also under
+ * stream capture).  Every launch is the one ROCS_EXEC_SHARED_SERIAL makes, so
+ * the two modes give identical bits.  Calls that overlap on one device share
+ * the internal stream (their request work runs in call order). */
 
 typedef enum rocs_op_kind {
   ROCS_OP_LINEAR = 1,    /* rocs_lcb_forward                                      */

@@ -28,7 +28,7 @@ ROCS_ERR_UNSUPPORTED = -8
 ROCS_F32, ROCS_BF16 = 0, 1
 ROCS_ACT_NONE, ROCS_ACT_RELU = 0, 1
 ROCS_NORM_LAYER, ROCS_NORM_RMS = 0, 1
-ROCS_EXEC_SHARED, ROCS_EXEC_DENSE_BROADCAST = 0, 1
+ROCS_EXEC_SHARED, ROCS_EXEC_DENSE_BROADCAST, ROCS_EXEC_SHARED_SERIAL = 0, 1, 2
 ROCS_OP_LINEAR, ROCS_OP_NORM, ROCS_OP_FM, ROCS_OP_TOKEN_LCB, ROCS_OP_XATTN, ROCS_OP_HEAD = 1, 2, 3, 4, 5, 6
 
 c_int32, c_int64, c_size_t, c_float, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p

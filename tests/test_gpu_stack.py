@@ -204,3 +204,86 @@ def test_head_fused_into_norm_matches_standalone_head(k):
                          Rr.cur_stream())
     torch.cuda.synchronize()
     assert np.array_equal(lg[: st.B_c].cpu().numpy(), out["logits"])
+
+
+# ------------------------------------------------------------------ two lanes
+
+@pytest.mark.parametrize("fusion", [False, True])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_two_lane_schedule_matches_serial_bitwise(k, fusion):
+    """ROCS_EXEC_SHARED puts the request rows' launches on an internal stream
+    (candidate launches wait on events for Z, the request dots and the keys
+    and values); ROCS_EXEC_SHARED_SERIAL makes the same launches on the
+    caller's stream.  The two give identical bits."""
+    from request_candidate_sharing_amd import rocs as R
+
+    inp = S.make_inputs(S.small_config(k))
+    _, a = _stack(inp, mode=R.ROCS_EXEC_SHARED, fusion=fusion)
+    _, b = _stack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL, fusion=fusion)
+    for key in ("y_c", "y_r", "logits"):
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_two_lane_calls_in_a_row_see_their_own_inputs():
+    """Back-to-back calls on one stream with inputs rewritten on that stream
+    between them (the request lane starts after the caller's earlier work,
+    the caller's stream waits for the request lane): every call equals a
+    serial call on the same inputs."""
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    base = S.make_inputs(S.small_config(5))
+    two = DeviceStack(base)
+    ser = DeviceStack(base, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    rng = np.random.default_rng(11)
+    for i in range(4):
+        xr = S.round_bf16(rng.standard_normal(two.x_r.shape).astype(np.float32))
+        xc = S.round_bf16(rng.standard_normal(two.x_c.shape).astype(np.float32))
+        for st in (two, ser):
+            st.x_r.copy_(torch.as_tensor(xr, device="cuda").to(st.x_r.dtype))
+            st.x_c.copy_(torch.as_tensor(xc, device="cuda").to(st.x_c.dtype))
+        two.run()
+        two.run()  # twice: the second call reuses the workspace behind the first
+        ser.run()
+        a, b = two.outputs(), ser.outputs()
+        for key in ("y_c", "y_r", "logits"):
+            if a[key] is not None:
+                assert np.array_equal(a[key], b[key]), (i, key)
+
+
+def test_two_lane_schedule_replays_from_a_graph():
+    """Captured into a graph (the internal stream joins the capture through
+    the fork event and leaves it through the join), every replay equals the
+    eager call, with eager calls of another stack between replays."""
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    inp = S.make_inputs(S.small_config(2))
+    st = DeviceStack(inp)
+    other = DeviceStack(S.make_inputs(S.small_config(2), seed=77))
+    st.run()
+    eager = st.outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    for i in range(3):
+        st.y_c.fill_(float("nan"))
+        st.y_r.fill_(float("nan"))
+        g.replay()
+        other.run()
+        got = st.outputs()
+        for key in ("y_c", "y_r", "logits"):
+            if eager[key] is not None:
+                assert np.array_equal(got[key], eager[key]), (i, key)
+
+
+def test_two_lane_full_size_matches_serial_bitwise():
+    """The benchmarked ranking stack (config 5) in both schedules: identical bits."""
+    from request_candidate_sharing_amd import rocs as R
+
+    inp = S.make_inputs(S.config(5))
+    _, a = _stack(inp, mode=R.ROCS_EXEC_SHARED)
+    _, b = _stack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    for key in ("y_c", "y_r", "logits"):
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
