@@ -518,14 +518,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uin
   store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc, reinterpret_cast<float*>(smem) + wave * stage_floats<FN>());
 }
 
-// One tile per workgroup, tiles in XCD-aware order.
+// One tile per workgroup, tiles in XCD-aware order.  A batch of GEMMs is
+// one flat grid of (GEMM, tile) pairs, remapped as a whole, so each XCD
+// runs a contiguous range of one GEMM's tiles (its weights stay in that
+// XCD's L2).
 template <int BM, int BN, int WM, int WN, int NS = 2>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a) {
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_big_kernel(GemmArgs a0) {
   __shared__ uint4 smem[NS * (BM + BN) * 8];
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = (a.M + BM - 1) / BM;
-  const int logical = xcd_remap(blockIdx.x, ntm * ntn);
-  gemm_tile<BM, BN, WM, WN, NS>(a, (logical / ntn) * BM, (logical % ntn) * BN, smem);
+  const int ntn = (a0.N + BN - 1) / BN;
+  const int ntm = (a0.M + BM - 1) / BM;
+  const int tiles = ntm * ntn;
+  const int logical = xcd_remap(blockIdx.x, tiles * (a0.batch > 1 ? a0.batch : 1));
+  // the division runs on the vector unit; the member's pointers must stay scalar
+  const int member = __builtin_amdgcn_readfirstlane(logical / tiles);
+  const int t = logical - member * tiles;
+  const GemmArgs a = batch_slice(a0, member);
+  gemm_tile<BM, BN, WM, WN, NS>(a, (t / ntn) * BM, (t % ntn) * BN, smem);
 }
 
 // Two tile heights in one launch: rows [0, M1) in 256-row tiles (whole
@@ -774,7 +782,8 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   // A batch runs as one launch (grid.y = GEMM) on the split-K kernel, whose
   // few tiles per GEMM leave most of the chip idle; any other kernel choice
   // runs the GEMMs one launch each.
-  if (a.batch > 1 && !(dt == BF16 && uses_splitk(a))) {
+  const bool big_batch = dt == BF16 && a.M >= 2048 && a.N > 128;
+  if (a.batch > 1 && !(dt == BF16 && uses_splitk(a)) && !big_batch) {
     for (int i = 0; i < a.batch; ++i) {
       GemmArgs b = batch_slice(args, i);
       b.batch = 1;
@@ -791,6 +800,11 @@ hipError_t launch_gemm(DType dt, const GemmArgs& args, hipStream_t s) {
   // 1024): half the operand traffic from L2 per FLOP.  One workgroup fits
   // per CU, so the tile heights are chosen to fill the rounds (cand_plan).
   if (a.M >= 2048) {
+    if (a.N > 128 && a.batch > 1) {  // one flat grid of every GEMM's 256 x 256 tiles
+      const long nwg = long((a.M + 255) / 256) * ((a.N + 255) / 256) * a.batch;
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, 2, 4>), dim3(nwg), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
     if (a.N > 128) {
       const CandPlan p = cand_plan(a.M, (a.N + 255) / 256);
       switch (p.h) {

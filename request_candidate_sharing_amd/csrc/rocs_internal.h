@@ -47,10 +47,10 @@ struct GemmArgs {
   int64_t ldres;
   int epi;  // epilogue variant, set by launch_gemm (callers leave it 0)
   // Optional batch of `batch` independent GEMMs of this shape: GEMM i reads
-  // A, W[*], bias, res and writes out0 at i times these byte strides (Z,
-  // out1 and zmap are shared).  0 or 1 = one GEMM.
+  // A, W[*], bias, res and writes out0 at i times these byte strides, and
+  // reads Z at i * sz floats (out1 and zmap are shared).  0 or 1 = one GEMM.
   int batch;
-  int64_t sA, sW, s0, sbias, sres;
+  int64_t sA, sW, s0, sbias, sres, sz;
 };
 
 // GEMM i of a batched launch (pointers advanced by i strides).
@@ -63,6 +63,7 @@ __host__ __device__ inline GemmArgs batch_slice(const GemmArgs& a, int i) {
     b.out0 = static_cast<char*>(a.out0) + i * a.s0;
     if (a.bias) b.bias = static_cast<const char*>(a.bias) + i * a.sbias;
     if (a.res) b.res = static_cast<const char*>(a.res) + i * a.sres;
+    if (a.z) b.z = a.z + i * a.sz;
   }
   return b;
 }
