@@ -310,11 +310,12 @@ typedef enum rocs_exec_mode {
   ROCS_EXEC_SHARED_SERIAL = 2    /* as ROCS_EXEC_SHARED, every launch on the caller's stream */
 } rocs_exec_mode;
 /* Schedule of ROCS_EXEC_SHARED with both row groups present and a DCA
- * descriptor ([R] §2.4: the request and candidate tiles share the GPU, the
- * dependency on the request contribution is a completion signal instead of a
- * kernel boundary; stacks without DCA, whose request side is the GLM request
- * GEMMs alone, run as ROCS_EXEC_SHARED_SERIAL): the request rows' work runs
- * on an internal stream of the device (created once
+ * descriptor of more than one depth ([R] §2.4: the request and candidate
+ * tiles share the GPU, the dependency on the request contribution is a
+ * completion signal instead of a kernel boundary; other stacks, with no
+ * request-only work to overlap across layers, run as
+ * ROCS_EXEC_SHARED_SERIAL): the request rows' work runs on an internal
+ * stream of the device (created once
  * per device at default priority, kept until the process ends) and the
  * candidate rows' work on the caller's stream.  A candidate launch that reads
  * a request result (Z, the request dots of the head, the keys and values of
@@ -322,7 +323,8 @@ typedef enum rocs_exec_mode {
  * internal stream starts after an event recorded on the caller's stream at
  * the call, and the caller's stream waits for the internal one at the end, so
  * to the caller the call is ordered on its stream as one unit (also under
- * stream capture).  Every launch is the one ROCS_EXEC_SHARED_SERIAL makes, so
+ * stream capture).  The encoder and the K/V projections are enqueued in
+ * stages, each before the first cross-attention that needs its output.  Every launch is the one ROCS_EXEC_SHARED_SERIAL makes, so
  * the two modes give identical bits.  Calls that overlap on one device share
  * the internal stream (their request work runs in call order). */
 

@@ -345,9 +345,14 @@ const void* encoder_output(const void* seq, void* workspace, int k, int rows, in
 // cand_only: project only the candidate keys and values, kv[j] = [K_C | V_C]
 // ([rows, 2d] per depth) for callers that compute the request side from S
 // itself (rocs_rqattn.hip); otherwise kv[j] = [K_R | V_R | K_C | V_C].
+// Encoder layers [from, to) (to < 0: all), then the K/V projections of the
+// depths whose source output S[depth_src] they complete: sources from + 1 ..
+// to, and source 0 (the sequence itself) when from == 0.  Stages run in
+// order on one stream; the default is the whole encoder.
 int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t ffn, const void* seq, int32_t n_enc,
                      const rocs_enc_layer* enc, int32_t n_depths, const int32_t* depth_src, const rocs_kv_w* kvw,
-                     void* kv, void* workspace, hipStream_t s, bool cand_only = false) {
+                     void* kv, void* workspace, hipStream_t s, bool cand_only = false, int from = 0, int to = -1) {
+  if (to < 0) to = n_enc;
   if (B_r == 0) return ROCS_OK;
   const int rows = B_r * L;
   char* w = reinterpret_cast<char*>(workspace);
@@ -364,7 +369,7 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
   w += align_up(size_t(rows) * size_t(ffn) * 2, 256);
   bf16* vt = reinterpret_cast<bf16*>(w);
 
-  for (int k = 0; k < n_enc; ++k) {
+  for (int k = from; k < to; ++k) {
     const rocs_enc_layer& e = enc[k];
     const void* Sin = S[k];
     ROCS_TRY(gemm_plain(Sin, d, rows, 3 * d, d, e.w_qkv, e.b_qkv, 0, nullptr, 0, qkv, 3 * d, s, "encoder qkv"));
@@ -394,6 +399,7 @@ int encode_kv_launch(int32_t B_r, int32_t L, int32_t d, int32_t n_heads, int32_t
   }
   const int nseg = cand_only ? 2 : 4;
   for (int j = 0; j < n_depths; ++j) {
+    if (depth_src[j] > to || (depth_src[j] <= from && !(from == 0 && depth_src[j] == 0))) continue;
     GemmArgs g{};
     g.M = rows;
     g.N = nseg * d;

@@ -212,9 +212,11 @@ def test_head_fused_into_norm_matches_standalone_head(k):
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_two_lane_schedule_matches_serial_bitwise(k, fusion):
     """ROCS_EXEC_SHARED puts the request rows' launches on an internal stream
-    (candidate launches wait on events for Z, the request dots and the keys
-    and values); ROCS_EXEC_SHARED_SERIAL makes the same launches on the
-    caller's stream.  The two give identical bits."""
+    for DCA stacks of several depths (config 5 here: three depths, encoder
+    stages before depths 1 and 2; candidate launches wait on events for Z,
+    the request dots and the keys and values); ROCS_EXEC_SHARED_SERIAL makes
+    the same launches on the caller's stream.  The two give identical bits
+    (the other configs run serially in both modes)."""
     from request_candidate_sharing_amd import rocs as R
 
     inp = S.make_inputs(S.small_config(k))
@@ -258,9 +260,9 @@ def test_two_lane_schedule_replays_from_a_graph():
     eager call, with eager calls of another stack between replays."""
     from request_candidate_sharing_amd.stacks import DeviceStack
 
-    inp = S.make_inputs(S.small_config(2))
+    inp = S.make_inputs(S.small_config(5))
     st = DeviceStack(inp)
-    other = DeviceStack(S.make_inputs(S.small_config(2), seed=77))
+    other = DeviceStack(S.make_inputs(S.small_config(5), seed=77))
     st.run()
     eager = st.outputs()
     g = torch.cuda.CUDAGraph()
