@@ -279,6 +279,31 @@ def copy_calibration(mib=1024, reps=5):
     log(f"copy calibration: {reps} copies of {mib} MiB")
 
 
+def copy_bandwidth():
+    """The practical HBM ceiling: a plain device copy (torch's copy kernel) at
+    stack-like sizes, two buffer pairs in alternation, bytes read + written."""
+    import torch
+
+    for mb in (64, 150, 512, 2048):
+        n = mb * (1 << 20) // 2
+        xs = [torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        ys = [torch.empty_like(xs[0]) for _ in range(2)]
+        for i in range(4):
+            ys[i % 2].copy_(xs[i % 2])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 40
+        e0.record()
+        for i in range(reps):
+            ys[i % 2].copy_(xs[i % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps / 1e3
+        print(json.dumps({"study": "copy_bw", "copy_MB": mb, "us": t * 1e6,
+                          "TBps_read_plus_write": 2 * n * 2 / t / 1e12}), flush=True)
+        del xs, ys
+
+
 def oracle_threads() -> int:
     """Threads of the BLAS pool the numpy oracle runs on."""
     try:
@@ -596,6 +621,7 @@ def main():
                     help="steps of the steady-state window timed after the contract's timed steps")
     ap.add_argument("--latency-steps", type=int, default=100)
     ap.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
+    ap.add_argument("--copy-bw", action="store_true", help="study: plain device copy bandwidth (the practical HBM ceiling)")
     ap.add_argument("--workload", type=int, default=5,
                     help="5 (default) is the benchmark line; 1-4 time another workload's stack (profiling aid)")
     ap.add_argument("--roofline-only", action="store_true",
@@ -624,6 +650,10 @@ def main():
     if args.copy_calib:
         torch.cuda.set_device(0)
         copy_calibration()
+        return
+    if args.copy_bw:
+        torch.cuda.set_device(0)
+        copy_bandwidth()
         return
 
     import rocs_synth as S
