@@ -39,6 +39,19 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   const uint32_t m0 = uint32_t(uintptr_t((lds_ptr_t)dst));
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
+// The same DMA from a wave-uniform base held in SGPRs plus a 32-bit per-lane
+// byte offset: no 64-bit address arithmetic on the vector unit per load.
+__device__ __forceinline__ void dma16_s(const char* base, uint32_t off, void* dst) {
+  const uint32_t m0 = uint32_t(uintptr_t((lds_ptr_t)dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+// A pointer whose value is the same in every lane, moved to SGPRs.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt,
 // lgkmcnt at their maxima)
 template <int N>
@@ -319,6 +332,10 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
 // fills 2 of the 8 1-KB pieces of each tile; lane i fetches the 16-byte
 // chunk that the row swizzle places at its LDS slot.
 constexpr int NST = 3;
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
 constexpr int DMA_PER_SLAB = 4;  // wave-instructions per slab per wave (2 K + 2 V)
 
 __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
@@ -340,41 +357,64 @@ __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
 
   // LDS entry (2*wave + j)*64 + lane of a tile is row r = (2*wave + j)*8 +
   // lane/8, slot lane%8, which holds global chunk (lane%8) ^ swz(r) of that
-  // row; swz(r) = (lane/8) ^ j.
+  // row; swz(r) = (lane/8) ^ j.  Each lane's source is a fixed byte offset
+  // from the slab's base (kept in SGPRs; the launcher checks that 64 rows of
+  // K and of V^T span less than 2 GiB).
   const int row0 = wave * 16 + (lane >> 3);  // j = 0; j = 1 adds 8
   const int chunk0 = (lane & 7) ^ ((lane >> 3) & 7);
   const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH;
-  const bf16* vsrc = a.vt + ((int64_t(t.group) * a.n_heads + t.h) * DH + row0) * a.ldvt;
-  const int64_t vstep = 8 * a.ldvt;
-  auto issue = [&](int slab, int stage) {
+  const char* kb_s = uniform_ptr(kbase);
+  const char* vb_s = uniform_ptr(a.vt + (int64_t(t.group) * a.n_heads + t.h) * DH * a.ldvt);
+  const int64_t kslab = int64_t(KC) * a.ldkv * 2;  // bytes between slabs of K rows
+  uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // keys past L read row L-1: their scores are masked and their P is 0
-      const int key = min(slab * KC + row0 + 8 * j, L - 1);
-      dma16(kbase + int64_t(key) * a.ldkv + (chunk0 ^ j) * 8, &sK[stage][(2 * wave + j) * 64]);
+  for (int j = 0; j < 2; ++j) {
+    koff[j] = uint32_t(((row0 + 8 * j) * a.ldkv + (chunk0 ^ j) * 8) * 2);
+    voff[j] = uint32_t(((row0 + 8 * j) * a.ldvt + (chunk0 ^ j) * 8) * 2);
+  }
+  auto issue = [&](int slab, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    if ((slab + 1) * KC <= L) {
+      const char* kb = kb_s + slab * kslab;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16_s(kb, koff[j], &sK[S][(2 * wave + j) * 64]);
+    } else {
+      // the ragged last slab: keys past L read row L-1 (their scores are
+      // masked and their P is 0)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int key = min(slab * KC + row0 + 8 * j, L - 1);
+        dma16(kbase + int64_t(key) * a.ldkv + (chunk0 ^ j) * 8, &sK[S][(2 * wave + j) * 64]);
+      }
     }
+    // V^T rows are zero-padded to a multiple of 64 keys
+    const char* vb = vb_s + slab * (KC * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dma16(vsrc + j * vstep + slab * KC + (chunk0 ^ j) * 8, &sV[stage][(2 * wave + j) * 64]);
+    for (int j = 0; j < 2; ++j) dma16_s(vb, voff[j], &sV[S][(2 * wave + j) * 64]);
   };
 
   // Every step issues one slab (the last one again once past the end), so
   // "this wave's DMA for slab sb has landed" is always vmcnt <= one slab.
-  issue(0, 0);
-  issue(min(1, nslab - 1), 1);
+  issue(0, Stage<0>{});
+  issue(min(1, nslab - 1), Stage<1>{});
   QState st;
   load_q(a, q_phys, q_ok, t.h, hl, st);
   // The compiler does not see the DMA on the load counter: make it wait for
   // the Q fragments here, once, rather than inside the loop at their first use.
   asm volatile("" : : "v"(st.qf[0]), "v"(st.qf[1]), "v"(st.qf[2]), "v"(st.qf[3]));
-  int cur = 0, nxt = 2;
-  for (int sb = 0; sb < nslab; ++sb) {
+  // Slab sb lives in stage sb % 3.  The loop is unrolled over the stages so
+  // that every LDS address is a lane offset plus a constant.
+  auto step = [&](int sb, auto stage) {
+    constexpr int CUR = decltype(stage)::value, NXT = (CUR + 2) % NST;
     wait_vmcnt<DMA_PER_SLAB>();
-    __syncthreads();  // slab sb is in LDS for all waves; stage nxt (slab sb-1) is free
-    issue(min(sb + 2, nslab - 1), nxt);
-    attend_slab(sK[cur], sV[cur], sb * KC, L, a.scale_log2, lane, st);
-    cur = cur == NST - 1 ? 0 : cur + 1;
-    nxt = nxt == NST - 1 ? 0 : nxt + 1;
+    __syncthreads();  // slab sb is in LDS for all waves; stage NXT (slab sb-1) is free
+    issue(min(sb + 2, nslab - 1), Stage<NXT>{});
+    attend_slab(sK[CUR], sV[CUR], sb * KC, L, a.scale_log2, lane, st);
+  };
+  for (int sb = 0; sb < nslab; sb += NST) {
+    step(sb, Stage<0>{});
+    if (sb + 1 < nslab) step(sb + 1, Stage<1>{});
+    if (sb + 2 < nslab) step(sb + 2, Stage<2>{});
   }
   wait_vmcnt<0>();  // no DMA may still write this workgroup's LDS when it exits
   if (q_ok) write_out(a, q_phys, t.h, hl, st);
@@ -634,8 +674,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int tiles = a.q_rows_per_group > 0 ? a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ) : a.max_tiles;
   if (tiles <= 0 || a.n_heads <= 0) return hipSuccess;
   if (a.L <= 0) return hipErrorInvalidValue;
-  if (a.vt != nullptr)
+  // attn_vt_kernel addresses 64 rows of K and of V^T by 32-bit offsets
+  const int64_t lim = int64_t(1) << 31;
+  const bool vt_ok = a.vt != nullptr && int64_t(KC) * a.ldkv * 2 < lim && int64_t(KC) * a.ldvt * 2 < lim;
+  if (vt_ok)
     hipLaunchKernelGGL(attn_vt_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  else if (a.v == nullptr)
+    return hipErrorInvalidValue;
   else
     hipLaunchKernelGGL(attn_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
   return hipGetLastError();
