@@ -412,6 +412,12 @@ struct SlabFeed {
     }
   }
   __device__ __forceinline__ void issue(int K, const void* zero, int k0, uint4* slot, int wave) const {
+    if (k0 + CPR * 8 <= K) {  // a whole slab inside K (a wave-uniform branch): no per-lane select
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)(slot + (wave * PER + j) * 64), 16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const void* p = (k0 + kofs[j] < K) ? static_cast<const void*>(src[j] + k0) : zero;
@@ -473,7 +479,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uin
   static_assert(NW * stage_floats<FN>() * 4 <= NS * SLOT * 16, "epilogue stage exceeds the ring");
   using Feed = SlabFeed<BM, BN, NW>;
   static_assert(NS >= 2 && Feed::PER * (NS - 2) < 64, "ring depth");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: the LDS slot addresses of the DMA stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const void* zero = pinned_zero_page();
   const WeightSegs ws = weight_segs(a);
