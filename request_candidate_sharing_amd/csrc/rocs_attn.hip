@@ -40,10 +40,17 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 // The same DMA from a wave-uniform base held in SGPRs plus a 32-bit per-lane
-// byte offset: no 64-bit address arithmetic on the vector unit per load.
+// byte offset: no 64-bit address arithmetic on the vector unit per load.  The
+// base is copied by the scalar unit first: a vector-memory read of an SGPR
+// written by a VALU instruction (v_readfirstlane, v_readlane) needs five wait
+// states, which the compiler does not insert for inline asm.
 __device__ __forceinline__ void dma16_s(const char* base, uint32_t off, void* dst) {
   const uint32_t m0 = uint32_t(uintptr_t((lds_ptr_t)dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0) : "memory");
+  uint64_t b;
+  asm volatile("s_mov_b64 %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0"
+               : "=&s"(b)
+               : "s"(base), "v"(off), "{m0}"(m0)
+               : "memory");
 }
 // A pointer whose value is the same in every lane, moved to SGPRs.
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
