@@ -97,8 +97,7 @@ def dca_costs(cfg):
 def dca_work(cfg, B_r, B_c):
     """Algorithmic FLOPs and bytes of one shared DCA stack step.  Bytes count
     each kernel's operands read once and outputs written once (weights once,
-    Z and K/V at request size, bf16 activations, fp32 Z); the V^T staging
-    copies are not algorithmic and are left out."""
+    Z and K/V at request size, bf16 activations, fp32 Z)."""
     C_R, C_C = dca_costs(cfg)
     F = B_r * C_R + B_c * C_C
     d, L, ffn, H = cfg.d_seq, cfg.L, cfg.ffn, cfg.hidden

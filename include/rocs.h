@@ -220,13 +220,13 @@ int rocs_dca_encode_kv(rocs_dtype dtype, int32_t B_r, int32_t L, int32_t d, int3
  * request share each staged key/value tile.  q_r [B_r, H*64] (ld_qr),
  * q_c [B_c, H*64] (ld_qc); outputs a_r (ld_ar), a_c (ld_ac).  q_r/a_r
  * nullable (skip the request group).  bf16 only, head_dim == 64,
- * scale <= 0 selects 1/sqrt(head_dim).  workspace >=
- * rocs_dca_cross_attn_workspace_size(B_r, B_c, n_heads, L): per-request
- * query tiles, a device counting sort of cand2req when batch->offsets is
- * NULL, and V_R^T / V_C^T staged once per call (keys contiguous per head
- * dimension, the layout the PV product reads), so that the query tiles of
- * one request do not each transpose the same values.  Needed whenever
- * there are candidates or request queries. */
+ * ld_kv < 2^24 (ROCS_ERR_UNSUPPORTED otherwise), scale <= 0 selects
+ * 1/sqrt(head_dim).  workspace >=
+ * rocs_dca_cross_attn_workspace_size(B_r, B_c, n_heads, L): the per-request
+ * query tiles and a device counting sort of cand2req when batch->offsets
+ * is NULL (the size depends on B_r and B_c only; n_heads and L are
+ * accepted for callers that size workspaces per layer).  Needed whenever
+ * there are candidates. */
 size_t rocs_dca_cross_attn_workspace_size(int32_t B_r, int32_t B_c, int32_t n_heads, int32_t L);
 int rocs_dca_cross_attn(const rocs_batch* batch, rocs_dtype dtype, int32_t n_heads, int32_t head_dim, int32_t L,
                         const void* q_r, int64_t ld_qr, const void* q_c, int64_t ld_qc, const void* k_r,
@@ -257,15 +257,13 @@ int rocs_dca_request_attn(rocs_dtype dtype, int32_t B_r, int32_t n_heads, int32_
 /* Variant of rocs_dca_cross_attn that allocates nothing and takes no
  * workspace, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
- * Same arguments, results and errors as rocs_dca_cross_attn except:
- * - its only scratch, the attention plan (per-request counts and offsets,
- *   the candidate permutation, the query tiles), lives in a static device
- *   array of ROCS_XATTN_NOALLOC_SCRATCH_BYTES per GPU, held until the
- *   process ends; a batch whose plan needs more (about 4 bytes per
- *   candidate plus 24 bytes per request) returns ROCS_ERR_WORKSPACE before
- *   anything is enqueued;
- * - V is transposed inside the attention kernel instead of being staged.
- * Every call on one GPU shares that GPU's array, which keeps the last
+ * Same arguments, results and errors as rocs_dca_cross_attn, except that
+ * its only scratch, the attention plan (per-request counts and offsets,
+ * the candidate permutation, the query tiles), lives in a static device
+ * array of ROCS_XATTN_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends; a batch whose plan needs more (about 4 bytes per candidate plus 24
+ * bytes per request) returns ROCS_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array, which keeps the last
  * call's contents (each call clears what must start at zero).  Calls that
  * overlap on one GPU (other streams, other host threads) race. */
 #define ROCS_XATTN_NOALLOC_SCRATCH_BYTES (4 << 20)

@@ -2,24 +2,22 @@
 // IKBO-DCA): keys/values stay at request-batch size and every query tile is
 // made of queries of ONE request, so each staged key/value tile in LDS is
 // shared by all the queries of the workgroup, and the tiles of one request
-// run back to back on one XCD (shared L2).  The same kernels run the
+// run back to back on one XCD (shared L2).  The same kernel runs the
 // request-only encoder's self-attention (group = one request's sequence).
 //
 // Per workgroup: 4 waves x 32 queries = 128 queries of one group and one
-// head (head_dim 64).  Keys stream in 64-key slabs through LDS (K row-major,
-// V transposed).  Each wave computes S^T = K Q^T with
+// head (head_dim 64).  Keys and values stream in 64-key slabs, as they are
+// stored (row-major key rows), global -> LDS by DMA through a 3-stage ring
+// (two slabs in flight).  Each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, so each lane holds scores of a single query:
 // the online-softmax max/sum need one exchange between lanes l and l ^ 32
 // per slab (v_permlane32_swap).  P^T is fed back as the B operand of
-// O^T = V^T P^T in the register order the S^T accumulator produced (the key
-// order inside one MFMA k-step only has to agree between the two operands;
-// the V^T rows are stored in that order).  Softmax in fp32 with exp2 and the
-// scale folded into one multiply-add; the running maximum is only moved when
-// a score exceeds it by more than 2^8 in exp2 units (lazy rescaling).
-//
-// With V^T staged once per call (vtrans_kernel), attn_vt_kernel feeds K and
-// V^T slabs by LDS DMA through a 3-stage ring (two slabs in flight); without
-// it, attn_kernel stages through registers and transposes V into LDS.
+// O^T = V^T P^T in the register order the S^T accumulator produced; the
+// V^T operand is read from the row-major value tile with transposing LDS
+// reads (ds_read_b64_tr_b16) in that same key order.  Softmax in fp32 with
+// exp2 and the scale folded into one multiply-add; the running maximum is
+// only moved when a score exceeds it by more than 2^8 in exp2 units (lazy
+// rescaling).
 #include "rocs_device.h"
 
 namespace rocs {
@@ -76,14 +74,8 @@ constexpr int DH = 64;   // head dim
 // hits distinct banks in every group of 16 lanes (256 B of banks per clock),
 // and in every group of 8.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-// K tile: [64 keys][64 dh] bf16.
+// K and V tiles: [64 keys][64 dh] bf16.
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chunk ^ swz(key)); }
-// V^T tile: [64 dh][64 keys] bf16.  Inside a row the keys sit in the order
-// the PV step consumes them: position = key with bits 2 and 3 exchanged, so
-// the 8 keys one lane feeds to one MFMA k-step (two runs of 4 keys, 8 apart)
-// are one 16-byte chunk.
-__device__ __forceinline__ int vt_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
-__device__ __forceinline__ int vt_chunk(int dh, int chunk) { return dh * 8 + (chunk ^ swz(dh)); }
 
 // Query tile of one workgroup: group (request / sequence), rows [rbeg, rend)
 // of the query batch, head h.  Returns false when the workgroup has no tile.
@@ -157,11 +149,38 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 4 x 16-bit words that lanes
+// 4k + i / 4 (k = 0..3) address, in that order of k.
+__device__ __forceinline__ v4s read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((__attribute__((address_space(3))) const char*)p));
+}
+
+// Byte offset, in a row-major [64 keys][64 dh] tile (k_off layout), of the
+// 4 x 16-bit word this lane addresses for the transposed V reads of head-dim
+// block dt (32 dh) and key run j.  Source lane 4k + g of 16-lane group G
+// addresses keys 8j + 4 hl + k (hl = G / 2) and dh 32 dt + 16 (G % 2) + 4g
+// .. +3, so output lane i of the group holds dh 32 dt + 16 (G % 2) + i for
+// the four keys 8j + 4 hl + 0..3: the A operand of O^T = V^T P^T for MFMA
+// rows (lane % 32) and the key order the P^T registers come in.  A slab's
+// key tile (32 kt + 16 sp) adds a multiple of 16 rows, which keeps the row
+// swizzle.
+__device__ __forceinline__ int vrow_off(int lane, int dt, int j) {
+  const int G = lane >> 4, k = (lane >> 2) & 3, g = lane & 3;
+  const int row = 8 * j + 4 * (G >> 1) + k;
+  const int chunk = 4 * dt + 2 * (G & 1) + (g >> 1);
+  return row * 128 + (chunk ^ swz(row)) * 16 + (g & 1) * 8;
+}
+
 // One 64-key slab for the wave's 32 queries: S^T = K Q^T, online softmax,
-// O^T += V^T P^T.  tK: [64 keys][8 chunks] (k_off), tV: [64 dh][8 chunks]
-// (vt_chunk, keys in vt_pos order); key0 = first key of the slab.
+// O^T += V^T P^T.  tK, tV: [64 keys][8 chunks] (k_off); tV is read
+// transposed (vo: vrow_off per dt, j).  key0 = first key of the slab.
 __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, int key0, int L, float c, int lane,
-                                            QState& st) {
+                                            QState& st, const int (&vo)[2][2]) {
   const int hl = lane >> 5;
   // All 8 K fragments first (their LDS latency overlaps), then the S MFMAs.
   uint4 kf[8];
@@ -189,7 +208,11 @@ __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, in
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int sp = 0; sp < 2; ++sp) vf[dt * 4 + kt * 2 + sp] = tV[vt_chunk(dt * 32 + (lane & 31), 4 * kt + 2 * sp + hl)];
+      for (int sp = 0; sp < 2; ++sp) {
+        const char* tb = reinterpret_cast<const char*>(tV) + (kt * 32 + 16 * sp) * 128;
+        const v4s lo = read_tr16(tb + vo[dt][0]), hi = read_tr16(tb + vo[dt][1]);
+        vf[dt * 4 + kt * 2 + sp] = __builtin_bit_cast(uint4, v8s(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+      }
   __builtin_amdgcn_sched_barrier(0);
   // mask keys beyond L (last slab only)
   if (key0 + KC > L) {
@@ -265,79 +288,12 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t q_phys, int
     }
 }
 
-// V read row-major from the K/V rows and transposed into LDS on the way in
-// (register-staged, one slab ahead).
-__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
-  __shared__ uint4 sK[2][KC * 8];
-  __shared__ uint4 sV[2][DH * 8];
-  QTile t;
-  if (!decode_tile(a, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
-  const int q_local = t.rbeg + wave * 32 + (lane & 31);
-  const bool q_ok = q_local < t.rend;
-  const int64_t q_phys = q_ok ? (a.perm ? a.perm[q_local] : q_local) : 0;
-  if (t.group >= a.n_groups) {
-    if (q_ok) write_nan_row(a, q_phys, t.h, hl);
-    return;
-  }
-  QState st;
-  load_q(a, q_phys, q_ok, t.h, hl, st);
-  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH;
-  const bf16* vbase = a.v + int64_t(t.group) * a.kv_group_stride + t.h * DH;
-  const int L = a.L;
-  const int nslab = (L + KC - 1) / KC;
-
-  // each thread stages 2 K chunks and 2 V chunks (16 B) per slab; keys past L
-  // are zeros
-  uint4 rk[2], rv[2];
-  auto gload = [&](int slab) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256;
-      const int key = id >> 3, cc = id & 7;
-      const int gk = slab * KC + key;
-      rk[i] = gk < L ? *reinterpret_cast<const uint4*>(kbase + int64_t(gk) * a.ldkv + cc * 8) : make_uint4(0, 0, 0, 0);
-      rv[i] = gk < L ? *reinterpret_cast<const uint4*>(vbase + int64_t(gk) * a.ldkv + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256;
-      const int key = id >> 3, cc = id & 7;
-      sK[buf][k_off(key, cc)] = rk[i];
-      // transpose V: dh = cc*8 + e
-      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rv[i]);
-      uint16_t* vt = reinterpret_cast<uint16_t*>(sV[buf]);
-      const int pos = vt_pos(key);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dh = cc * 8 + e;
-        vt[vt_chunk(dh, pos >> 3) * 8 + (pos & 7)] = e16[e];
-      }
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int sb = 0; sb < nslab; ++sb) {
-    const int cur = sb & 1;
-    const bool more = sb + 1 < nslab;
-    if (more) gload(sb + 1);
-    attend_slab(sK[cur], sV[cur], sb * KC, L, a.scale_log2, lane, st);
-    if (more) sstore(cur ^ 1);
-    __syncthreads();
-  }
-  if (q_ok) write_out(a, q_phys, t.h, hl, st);
-}
-
-// V^T staged by vtrans_kernel (rows of keys in vt_pos order, zero-padded to
-// a multiple of 64).  K and V^T slabs move global -> LDS by DMA
-// (global_load_lds_dwordx4) through a ring of NST stages, so two slabs are in
-// flight while one is consumed and no registers hold staged data.  Each wave
-// fills 2 of the 8 1-KB pieces of each tile; lane i fetches the 16-byte
-// chunk that the row swizzle places at its LDS slot.
+// K and V slabs move global -> LDS by DMA (global_load_lds_dwordx4) through
+// a ring of NST stages, so two slabs are in flight while one is consumed and
+// no registers hold staged data.  Both tiles are row-major key rows in the
+// k_off layout (V is read transposed by the PV step).  Each wave fills 2 of
+// the 8 1-KB pieces of each tile; lane i fetches the 16-byte chunk that the
+// row swizzle places at its LDS slot.
 constexpr int NST = 3;
 template <int S>
 struct Stage {
@@ -345,9 +301,9 @@ struct Stage {
 };
 constexpr int DMA_PER_SLAB = 4;  // wave-instructions per slab per wave (2 K + 2 V)
 
-__global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
   __shared__ uint4 sK[NST][KC * 8];
-  __shared__ uint4 sV[NST][DH * 8];
+  __shared__ uint4 sV[NST][KC * 8];
   QTile t;
   if (!decode_tile(a, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
@@ -365,39 +321,42 @@ __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
   // LDS entry (2*wave + j)*64 + lane of a tile is row r = (2*wave + j)*8 +
   // lane/8, slot lane%8, which holds global chunk (lane%8) ^ swz(r) of that
   // row; swz(r) = (lane/8) ^ j.  Each lane's source is a fixed byte offset
-  // from the slab's base (kept in SGPRs; the launcher checks that 64 rows of
-  // K and of V^T span less than 2 GiB).
+  // from the slab's base (kept in SGPRs; the launcher checks that 64 key
+  // rows span less than 2 GiB).  K and V rows share the stride and offsets.
   const int row0 = wave * 16 + (lane >> 3);  // j = 0; j = 1 adds 8
   const int chunk0 = (lane & 7) ^ ((lane >> 3) & 7);
-  const bf16* kbase = a.k + int64_t(t.group) * a.kv_group_stride + t.h * DH;
+  const int64_t gofs = int64_t(t.group) * a.kv_group_stride + t.h * DH;
+  const bf16* kbase = a.k + gofs;
+  const bf16* vbase = a.v + gofs;
   const char* kb_s = uniform_ptr(kbase);
-  const char* vb_s = uniform_ptr(a.vt + (int64_t(t.group) * a.n_heads + t.h) * DH * a.ldvt);
-  const int64_t kslab = int64_t(KC) * a.ldkv * 2;  // bytes between slabs of K rows
-  uint32_t koff[2], voff[2];
+  const char* vb_s = uniform_ptr(vbase);
+  const int64_t kslab = int64_t(KC) * a.ldkv * 2;  // bytes between slabs of key rows
+  uint32_t koff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    koff[j] = uint32_t(((row0 + 8 * j) * a.ldkv + (chunk0 ^ j) * 8) * 2);
-    voff[j] = uint32_t(((row0 + 8 * j) * a.ldvt + (chunk0 ^ j) * 8) * 2);
-  }
+  for (int j = 0; j < 2; ++j) koff[j] = uint32_t(((row0 + 8 * j) * a.ldkv + (chunk0 ^ j) * 8) * 2);
+  int vo[2][2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vo[dt][j] = vrow_off(lane, dt, j);
   auto issue = [&](int slab, auto stage) {
     constexpr int S = decltype(stage)::value;
     if ((slab + 1) * KC <= L) {
-      const char* kb = kb_s + slab * kslab;
+      const int64_t so = slab * kslab;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16_s(kb, koff[j], &sK[S][(2 * wave + j) * 64]);
+      for (int j = 0; j < 2; ++j) dma16_s(kb_s + so, koff[j], &sK[S][(2 * wave + j) * 64]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16_s(vb_s + so, koff[j], &sV[S][(2 * wave + j) * 64]);
     } else {
       // the ragged last slab: keys past L read row L-1 (their scores are
-      // masked and their P is 0)
+      // masked, so their P is 0 and the finite V row adds nothing)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int key = min(slab * KC + row0 + 8 * j, L - 1);
-        dma16(kbase + int64_t(key) * a.ldkv + (chunk0 ^ j) * 8, &sK[S][(2 * wave + j) * 64]);
+        const int64_t o = int64_t(min(slab * KC + row0 + 8 * j, L - 1)) * a.ldkv + (chunk0 ^ j) * 8;
+        dma16(kbase + o, &sK[S][(2 * wave + j) * 64]);
+        dma16(vbase + o, &sV[S][(2 * wave + j) * 64]);
       }
     }
-    // V^T rows are zero-padded to a multiple of 64 keys
-    const char* vb = vb_s + slab * (KC * 2);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16_s(vb, voff[j], &sV[S][(2 * wave + j) * 64]);
   };
 
   // Every step issues one slab (the last one again once past the end), so
@@ -416,7 +375,7 @@ __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
     wait_vmcnt<DMA_PER_SLAB>();
     __syncthreads();  // slab sb is in LDS for all waves; stage NXT (slab sb-1) is free
     issue(min(sb + 2, nslab - 1), Stage<NXT>{});
-    attend_slab(sK[CUR], sV[CUR], sb * KC, L, a.scale_log2, lane, st);
+    attend_slab(sK[CUR], sV[CUR], sb * KC, L, a.scale_log2, lane, st, vo);
   };
   for (int sb = 0; sb < nslab; sb += NST) {
     step(sb, Stage<0>{});
@@ -425,41 +384,6 @@ __global__ __launch_bounds__(256, 3) void attn_vt_kernel(AttnArgs a) {
   }
   wait_vmcnt<0>();  // no DMA may still write this workgroup's LDS when it exits
   if (q_ok) write_out(a, q_phys, t.h, hl, st);
-}
-
-// ----------------------------------------------------------------- V^T staging
-// The PV product takes V^T (keys contiguous per head dimension) as its A
-// operand.  Transposed once per call here (one 64-key block of one head of
-// one sequence per workgroup), every query tile then loads V^T rows with
-// 16-byte loads instead of transposing the same V in LDS again.
-__global__ __launch_bounds__(256) void vtrans_kernel(const bf16* __restrict__ v, int64_t ldv, int64_t gstride, int L,
-                                                     int H, int64_t Lp, bf16* __restrict__ vt) {
-  __shared__ uint16_t t[KC][DH + 2];  // [key][e]
-  const int kb = blockIdx.x, h = blockIdx.y, g = blockIdx.z;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int id = tid + i * 256;
-    const int key = id >> 3, c = id & 7;
-    const int gk = kb * KC + key;
-    const uint4 u = gk < L ? *reinterpret_cast<const uint4*>(v + g * gstride + int64_t(gk) * ldv + h * DH + c * 8)
-                           : make_uint4(0, 0, 0, 0);
-    const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[key][c * 8 + e] = e16[e];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int id = tid + i * 256;
-    const int e = id >> 3, c = id & 7;
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = uint32_t(t[vt_pos(c * 8 + 2 * j)][e]) | (uint32_t(t[vt_pos(c * 8 + 2 * j + 1)][e]) << 16);
-    *reinterpret_cast<uint4*>(vt + ((int64_t(g) * H + h) * DH + e) * Lp + kb * KC + c * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
 }
 
 // ----------------------------------------------------------------- planning
@@ -681,24 +605,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int tiles = a.q_rows_per_group > 0 ? a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ) : a.max_tiles;
   if (tiles <= 0 || a.n_heads <= 0) return hipSuccess;
   if (a.L <= 0) return hipErrorInvalidValue;
-  // attn_vt_kernel addresses 64 rows of K and of V^T by 32-bit offsets
-  const int64_t lim = int64_t(1) << 31;
-  const bool vt_ok = a.vt != nullptr && int64_t(KC) * a.ldkv * 2 < lim && int64_t(KC) * a.ldvt * 2 < lim;
-  if (vt_ok)
-    hipLaunchKernelGGL(attn_vt_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
-  else if (a.v == nullptr)
-    return hipErrorInvalidValue;
-  else
-    hipLaunchKernelGGL(attn_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  // the kernel addresses 64 key rows by 32-bit byte offsets
+  if (a.ldkv >= kMaxAttnLdkv) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_dma_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_vtrans(const bf16* v, int64_t ldv, int64_t gstride, int G, int H, int L, bf16* vt, hipStream_t s) {
-  if (G <= 0 || H <= 0 || L <= 0) return hipSuccess;
-  const int64_t Lp = vt_pad(L);
-  hipLaunchKernelGGL(vtrans_kernel, dim3(unsigned(Lp / KC), unsigned(H), unsigned(G)), dim3(256), 0, s, v, ldv,
-                     gstride, L, H, Lp, vt);
-  return hipGetLastError();
-}
 
 }  // namespace rocs

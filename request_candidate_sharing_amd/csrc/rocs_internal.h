@@ -145,17 +145,11 @@ struct AttnArgs {
   const int32_t* n_tiles_dev;
   const int32_t* perm;  // optional row permutation: logical row r is physical row perm[r]
   int max_tiles;
-  // optional V^T staging (launch_vtrans, layout below); when set, v is not read
-  const bf16* vt;
-  int64_t ldvt;
 };
+// hipErrorInvalidValue when ldkv >= 2^24 (64 key rows are addressed by
+// 32-bit byte offsets) or L <= 0
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
-// V^T staging: row (g*H + h)*64 + e of vt (Lp = round_up(L, 64) elements) holds
-// v[g*gstride + key*ldv + h*64 + e] for keys < L and 0 for L <= key < Lp, with
-// key at position 64*(key/64) + p(key%64), p exchanging bits 2 and 3 (the key
-// order the attention kernels' PV step consumes).
-hipError_t launch_vtrans(const bf16* v, int64_t ldv, int64_t gstride, int G, int H, int L, bf16* vt, hipStream_t s);
-inline int64_t vt_pad(int L) { return (int64_t(L) + 63) / 64 * 64; }
+constexpr int64_t kMaxAttnLdkv = int64_t(1) << 24;
 int attn_tile_rows();
 
 // Builds per-request query tiles (and, without offsets, a counting sort of

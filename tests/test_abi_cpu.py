@@ -189,6 +189,18 @@ def test_stack_forward_checks_workspace_before_launch():
     assert st == R.ROCS_ERR_WORKSPACE
 
 
+def test_cross_attention_rejects_key_row_strides_past_2_pow_24():
+    # the attention kernel addresses 64 key rows by 32-bit byte offsets
+    b = R.batch(2, 4, None, FAKE)
+    args = (b, R.ROCS_BF16, 2, 64, 32, FAKE, 128, FAKE, 128, FAKE, FAKE, FAKE, FAKE)
+    tail = (0.125, FAKE, 128, FAKE, 128)
+    st = R.rocs_dca_cross_attn_noalloc(*args, 1 << 24, *tail, check=False)
+    assert st == R.ROCS_ERR_UNSUPPORTED
+    assert "2^24" in R.last_error()
+    st = R.rocs_dca_cross_attn(*args, 1 << 24, *tail, FAKE, 1 << 20, check=False)
+    assert st == R.ROCS_ERR_UNSUPPORTED
+
+
 def test_binding_raises_with_message():
     with pytest.raises(R.RocsError) as e:
         R.rocs_lcb_request(R.ROCS_BF16, 4, None, 64, 64, FAKE, FAKE, None, 64, 64, 0, None, 0, FAKE, 64, FAKE, 64)
