@@ -70,10 +70,14 @@ constexpr int KC = 64;   // keys per slab
 constexpr int DH = 64;   // head dim
 
 // Tiles hold 8 16-byte chunks per 128-byte row; chunk c of row r sits at
-// c ^ swz(r).  A fragment read (32 consecutive rows, one chunk column) then
-// hits distinct banks in every group of 16 lanes (256 B of banks per clock),
-// and in every group of 8.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// c ^ swz(r), with swz(r) = (r1 << 2) | ((r0 ^ r3) << 1) | r2 for the bits
+// r0..r3 of r.  Both LDS read patterns then hit distinct banks whether the
+// LDS serves 128 or 256 bytes per clock: the K fragment reads (32
+// consecutive rows, one chunk column; swz is a permutation over any 8
+// aligned rows, and over the 8 rows of one parity in 16) and the transposed
+// V reads (4 consecutive rows x 2 chunks per 16 lanes; swz bits 1-2 differ
+// between the 4 rows, and bit 2 flips between rows 2 apart).
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1); }
 // K and V tiles: [64 keys][64 dh] bf16.
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chunk ^ swz(key)); }
 
@@ -320,11 +324,13 @@ __global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
 
   // LDS entry (2*wave + j)*64 + lane of a tile is row r = (2*wave + j)*8 +
   // lane/8, slot lane%8, which holds global chunk (lane%8) ^ swz(r) of that
-  // row; swz(r) = (lane/8) ^ j.  Each lane's source is a fixed byte offset
-  // from the slab's base (kept in SGPRs; the launcher checks that 64 key
-  // rows span less than 2 GiB).  K and V rows share the stride and offsets.
+  // row.  Each lane's source is a fixed byte offset from the slab's base
+  // (kept in SGPRs; the launcher checks that 64 key rows span less than
+  // 2 GiB).  K and V rows share the stride and offsets.
   const int row0 = wave * 16 + (lane >> 3);  // j = 0; j = 1 adds 8
-  const int chunk0 = (lane & 7) ^ ((lane >> 3) & 7);
+  int chunk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) chunk[j] = (lane & 7) ^ swz(row0 + 8 * j);
   const int64_t gofs = int64_t(t.group) * a.kv_group_stride + t.h * DH;
   const bf16* kbase = a.k + gofs;
   const bf16* vbase = a.v + gofs;
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
   const int64_t kslab = int64_t(KC) * a.ldkv * 2;  // bytes between slabs of key rows
   uint32_t koff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) koff[j] = uint32_t(((row0 + 8 * j) * a.ldkv + (chunk0 ^ j) * 8) * 2);
+  for (int j = 0; j < 2; ++j) koff[j] = uint32_t(((row0 + 8 * j) * a.ldkv + chunk[j] * 8) * 2);
   int vo[2][2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
       // masked, so their P is 0 and the finite V row adds nothing)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t o = int64_t(min(slab * KC + row0 + 8 * j, L - 1)) * a.ldkv + (chunk0 ^ j) * 8;
+        const int64_t o = int64_t(min(slab * KC + row0 + 8 * j, L - 1)) * a.ldkv + chunk[j] * 8;
         dma16(kbase + o, &sK[S][(2 * wave + j) * 64]);
         dma16(vbase + o, &sV[S][(2 * wave + j) * 64]);
       }
