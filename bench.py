@@ -377,6 +377,10 @@ def other_workload(args):
     t_se, _ = time_steps(ser.run, args.steps, args.warmup)
     del ser
     out["serial_schedule_ms_per_step"] = t_se / args.steps * 1e3
+    fu = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    t_fu, _ = time_steps(fu.run, args.steps, args.warmup)
+    del fu
+    out["fused_glm_ms_per_step"] = t_fu / args.steps * 1e3
     if not args.no_dense:
         de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
         t_de, _ = time_steps(de.run, args.steps, args.warmup)
@@ -519,6 +523,60 @@ def ugsep_study(args):
     print(json.dumps(out), flush=True)
 
 
+def fused_glm_study(args):
+    """One GLM linear as one launch (request and candidate tiles in one grid,
+    completion counters) against the request and candidate launches, on the
+    GLM MLP stack's two linears at full size (256 requests, 73,704
+    candidates): 512 -> [1024 | 1024] with ReLU, and 1024 -> [512 | 512] with
+    a residual.  Both calls write the same bits (checked here)."""
+    import torch
+    import rocs_synth as S
+    from request_candidate_sharing_amd import rocs as R
+
+    cfg = S.config(2)
+    inp = S.make_inputs(cfg)
+    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
+    off = torch.as_tensor(inp["offsets"], device="cuda")
+    c2r = torch.as_tensor(inp["cand2req"], device="cuda")
+    batch = R.batch(B_r, B_c, off, c2r)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+    rn = lambda *sh, sc=1.0: (torch.randn(*sh, device="cuda", generator=g) * sc).to(bf)
+    st = R.cur_stream()
+    ws = torch.empty(R.rocs_lcb_fused_workspace_size(B_r), dtype=torch.uint8, device="cuda")
+    for name, K, N, act, res in (("up 512 -> 1024, ReLU", 512, 1024, R.ROCS_ACT_RELU, False),
+                                 ("down 1024 -> 512, residual", 1024, 512, R.ROCS_ACT_NONE, True)):
+        x_r, x_c = rn(B_r, K), rn(B_c, K)
+        w_rr, w_cr, w_cc = rn(N, K, sc=K ** -0.5), rn(N, K, sc=K ** -0.5), rn(N, K, sc=K ** -0.5)
+        b_r, b_c = rn(N, sc=0.5), rn(N, sc=0.5)
+        r_r, r_c = (rn(B_r, N), rn(B_c, N)) if res else (None, None)
+        outs = {}
+        for mode in ("two", "one"):
+            y_r, y_c = torch.empty(B_r, N, dtype=bf, device="cuda"), torch.empty(B_c, N, dtype=bf, device="cuda")
+            z = torch.empty(B_r, N, dtype=torch.float32, device="cuda")
+            a = (batch, R.ROCS_BF16, x_r, K, K, x_c, K, K, w_rr, w_cr, w_cc, b_r, b_c, N, N, act, r_r,
+                 N if res else 0, r_c, N if res else 0, y_r, N, y_c, N, z, N)
+            if mode == "two":
+                fn = lambda: R.rocs_lcb_forward(*a, st)
+            else:
+                fn = lambda: R.rocs_lcb_forward_fused(*a, ws, ws.numel(), st)
+            for _ in range(args.warmup * 4):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(args.steps * 5, 100)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            outs[mode] = (e0.elapsed_time(e1) * 1e3 / reps, y_r.clone(), y_c.clone(), z.clone())
+        same = all(torch.equal(outs["two"][i], outs["one"][i]) for i in (1, 2, 3))
+        print(json.dumps({"study": "fused_glm", "layer": name, "B_r": B_r, "B_c": B_c,
+                          "two_launches_us": outs["two"][0], "one_launch_us": outs["one"][0],
+                          "same_bits": bool(same)}), flush=True)
+
+
 def w8a16_study(args):
     """Latency of the W8A16 linear layer against the bf16 GEMM of the same
     shape, at the layer shapes of the UG-Separation page's W8A16 table.
@@ -595,6 +653,11 @@ def glm_stack_line(args):
     t_se, _ = time_steps(ser.run, args.steps, args.warmup)
     del ser
     out["serial_schedule_ms_per_step"] = t_se / args.steps * 1e3
+    # each GLM linear's request and candidate tiles in one launch
+    fu = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    t_fu, _ = time_steps(fu.run, args.steps, args.warmup)
+    del fu
+    out["fused_glm_ms_per_step"] = t_fu / args.steps * 1e3
     if not args.no_dense:
         de = DeviceStack(inp, mode=R.ROCS_EXEC_DENSE_BROADCAST)
         t_de, _ = time_steps(de.run, args.steps, args.warmup)
@@ -633,6 +696,8 @@ def main():
                     help="the UG-Separation TokenMixer workload (shared vs dense comparator), one JSON line")
     ap.add_argument("--w8a16", action="store_true",
                     help="W8A16 linear vs the bf16 GEMM at the UG-Separation page's W8A16 shapes, one JSON line each")
+    ap.add_argument("--fused-glm", action="store_true",
+                    help="study: a GLM linear as one launch vs two launches (GLM MLP stack shapes)")
     ap.add_argument("--order", action="store_true",
                     help="study: contiguous vs shuffled candidate order on workloads 2-5")
     ap.add_argument("--shuffle", action="store_true",
@@ -668,6 +733,8 @@ def main():
         return ugsep_study(args)
     if args.w8a16:
         return w8a16_study(args)
+    if args.fused_glm:
+        return fused_glm_study(args)
     if args.workload != 5:
         return other_workload(args)
 
@@ -732,6 +799,12 @@ def main():
     del ser
     out["serial_schedule"] = {"ms_per_step": t_se / args.steps * 1e3, "two_lane_saving_ms": t_se / args.steps * 1e3 - ms}
     log(f"bench: serial schedule {t_se / args.steps * 1e3:.3f} ms/step")
+    # serial, with each GLM linear's request and candidate tiles in one launch
+    fu = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    t_fu, _ = time_steps(fu.run, args.steps, args.warmup)
+    del fu
+    out["fused_glm_schedule"] = {"ms_per_step": t_fu / args.steps * 1e3}
+    log(f"bench: fused GLM schedule {t_fu / args.steps * 1e3:.3f} ms/step")
     if dense_out is not None:
         out["dense_broadcast"] = dense_out
         out["speedup_vs_dense_broadcast"] = dense_out["ms_per_step"] / ms

@@ -126,6 +126,30 @@ int rocs_lcb_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r,
                      rocs_act act, const void* res_r, int64_t ld_resr, const void* res_c, int64_t ld_resc,
                      void* y_r, int64_t ld_yr, void* y_c, int64_t ld_yc, float* z, int64_t ld_z, void* stream);
 
+/* rocs_lcb_forward as one launch ([R] §2.4: the request and candidate tiles
+ * of the LCB in one mega-kernel, the dependency on z a completion flag
+ * instead of a kernel boundary; §3.5 Table 4, last step).  Same arguments and
+ * outputs, bit-identical to rocs_lcb_forward, plus a workspace of at least
+ * rocs_lcb_fused_workspace_size(B_r) bytes (caller-owned, 16-byte aligned,
+ * contents arbitrary; the call zeroes the completion counters in it first,
+ * one small launch, and the fused launch follows on the same stream; calls
+ * that share a workspace must be ordered on one stream).  The request tiles
+ * take the lowest workgroup ids; a candidate tile polls the counters of the
+ * 32-row request blocks its map entries name before it reads z.  A poll
+ * gives up after a bounded number of tries (it cannot be reached while
+ * workgroups dispatch in id order); the tile's outputs are then NaN.
+ * Returns ROCS_ERR_UNSUPPORTED, having enqueued nothing, unless dtype is
+ * bf16, 0 < B_r < 2048, B_c >= 2048, d_out_c > 128 and a multiple of 256,
+ * at most one of ReLU and res_c is used, and every row offset of y_c, res_c
+ * and z fits in 31 bits. */
+size_t rocs_lcb_fused_workspace_size(int32_t B_r);
+int rocs_lcb_forward_fused(const rocs_batch* batch, rocs_dtype dtype, const void* x_r, int64_t ld_xr,
+                           int32_t d_in_r, const void* x_c, int64_t ld_xc, int32_t d_in_c, const void* w_rr,
+                           const void* w_cr, const void* w_cc, const void* b_r, const void* b_c, int32_t d_out_r,
+                           int32_t d_out_c, rocs_act act, const void* res_r, int64_t ld_resr, const void* res_c,
+                           int64_t ld_resc, void* y_r, int64_t ld_yr, void* y_c, int64_t ld_yc, float* z,
+                           int64_t ld_z, void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ scalar head
  * The GLM linear of [R] §2.1 with d_out_r = 0 and d_out_c = 1 (a candidate
  * score): z[b] = w_cr . x_r[b];  logits[i] = w_cc . x_c[i] + z[m_i] + bias.
@@ -305,8 +329,23 @@ int rocs_broadcast_rows(const rocs_batch* batch, int64_t row_bytes, const void* 
 typedef enum rocs_exec_mode {
   ROCS_EXEC_SHARED = 0,          /* request work at B_r size, map resolved in-kernel */
   ROCS_EXEC_DENSE_BROADCAST = 1, /* comparator: request contributions and K/V copied to B_c rows first */
-  ROCS_EXEC_SHARED_SERIAL = 2    /* as ROCS_EXEC_SHARED, every launch on the caller's stream */
+  ROCS_EXEC_SHARED_SERIAL = 2,   /* as ROCS_EXEC_SHARED, every launch on the caller's stream */
+  ROCS_EXEC_SHARED_FUSED = 3     /* as ROCS_EXEC_SHARED_SERIAL, each GLM linear's two halves in one launch */
 } rocs_exec_mode;
+/* ROCS_EXEC_SHARED_FUSED ([R] §2.4: request and candidate tiles in one
+ * mega-kernel, the dependency on the request contribution a completion flag
+ * instead of a kernel boundary; §3.5 Table 4, last step): every launch on the
+ * caller's stream, and a GLM linear whose request and candidate GEMMs fit
+ * one launch runs them as one grid.  Such a linear needs bf16, B_r < 2048,
+ * B_c >= 2048, d_out_c > 128 and a multiple of 256, d_out_c + d_out_r split
+ * as in rocs_lcb_forward, and at most one of ReLU and a residual (the
+ * candidate epilogue with Z in the accumulators); other layers make the
+ * launches of ROCS_EXEC_SHARED_SERIAL.  The request tiles take the lowest
+ * workgroup ids (dispatched first, they wait for nothing); a candidate tile
+ * polls one completion counter per 32 request rows it reads, in the
+ * workspace, zeroed once at the start of the call.  A poll gives up after a
+ * bounded number of tries; the tile's outputs are then NaN.  Outputs are
+ * bit-identical to ROCS_EXEC_SHARED_SERIAL. */
 /* Schedule of ROCS_EXEC_SHARED with both row groups present and a DCA
  * descriptor of more than one depth ([R] §2.4: the request and candidate
  * tiles share the GPU, the dependency on the request contribution is a

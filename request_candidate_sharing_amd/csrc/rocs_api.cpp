@@ -146,11 +146,10 @@ int lcb_request_check(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_xr
   return ROCS_OK;
 }
 
-int lcb_request_launch(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_xr, int32_t d_in_r, const void* w_rr,
-                       const void* w_cr, const void* b_r, int32_t d_out_r, int32_t d_out_c, int act,
-                       const void* res_r, int64_t ld_resr, void* y_r, int64_t ld_yr, float* z, int64_t ld_z,
-                       hipStream_t s, int64_t ldw = 0) {
-  if (B_r == 0 || d_out_r + d_out_c == 0) return ROCS_OK;
+GemmArgs lcb_request_args(int32_t B_r, const void* x_r, int64_t ld_xr, int32_t d_in_r, const void* w_rr,
+                          const void* w_cr, const void* b_r, int32_t d_out_r, int32_t d_out_c, int act,
+                          const void* res_r, int64_t ld_resr, void* y_r, int64_t ld_yr, float* z, int64_t ld_z,
+                          int64_t ldw = 0) {
   GemmArgs g{};
   g.M = B_r;
   g.N = d_out_r + d_out_c;
@@ -178,6 +177,16 @@ int lcb_request_launch(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_x
   g.act = act;
   g.res = res_r;
   g.ldres = ld_resr;
+  return g;
+}
+
+int lcb_request_launch(rocs_dtype dt, int32_t B_r, const void* x_r, int64_t ld_xr, int32_t d_in_r, const void* w_rr,
+                       const void* w_cr, const void* b_r, int32_t d_out_r, int32_t d_out_c, int act,
+                       const void* res_r, int64_t ld_resr, void* y_r, int64_t ld_yr, float* z, int64_t ld_z,
+                       hipStream_t s, int64_t ldw = 0) {
+  if (B_r == 0 || d_out_r + d_out_c == 0) return ROCS_OK;
+  const GemmArgs g = lcb_request_args(B_r, x_r, ld_xr, d_in_r, w_rr, w_cr, b_r, d_out_r, d_out_c, act, res_r, ld_resr,
+                                      y_r, ld_yr, z, ld_z, ldw);
   ROCS_HIP(launch_gemm(DType(dt), g, s), "rocs_lcb_request");
   return ROCS_OK;
 }
@@ -595,6 +604,41 @@ int rocs_lcb_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r,
                               res_r, ld_resr, y_r, ld_yr, z, ld_z, s));
   ROCS_TRY(lcb_candidate_launch(batch->num_candidates, batch->num_requests, batch->cand2req, dtype, x_c, ld_xc,
                                 d_in_c, w_cc, b_c, d_out_c, act, z, ld_z, res_c, ld_resc, y_c, ld_yc, s));
+  return ok();
+}
+
+size_t rocs_lcb_fused_workspace_size(int32_t B_r) {
+  return B_r > 0 ? align_up(size_t((B_r + 31) / 32 + 1) * 4, 256) : 256;
+}
+
+int rocs_lcb_forward_fused(const rocs_batch* batch, rocs_dtype dtype, const void* x_r, int64_t ld_xr,
+                           int32_t d_in_r, const void* x_c, int64_t ld_xc, int32_t d_in_c, const void* w_rr,
+                           const void* w_cr, const void* w_cc, const void* b_r, const void* b_c, int32_t d_out_r,
+                           int32_t d_out_c, rocs_act act, const void* res_r, int64_t ld_resr, const void* res_c,
+                           int64_t ld_resc, void* y_r, int64_t ld_yr, void* y_c, int64_t ld_yc, float* z,
+                           int64_t ld_z, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "rocs_lcb_forward_fused";
+  ROCS_TRY(check_batch(batch, fn));
+  ROCS_TRY(lcb_request_check(dtype, batch->num_requests, x_r, ld_xr, d_in_r, w_rr, w_cr, b_r, d_out_r, d_out_c, act,
+                             res_r, ld_resr, y_r, ld_yr, z, ld_z, fn));
+  ROCS_TRY(lcb_candidate_check(batch, dtype, x_c, ld_xc, d_in_c, w_cc, b_c, d_out_c, act, z, ld_z, res_c, ld_resc,
+                               y_c, ld_yc, fn));
+  const int B_r = batch->num_requests, B_c = batch->num_candidates;
+  const GemmArgs rq = lcb_request_args(B_r, x_r, ld_xr, d_in_r, w_rr, w_cr, b_r, d_out_r, d_out_c, act, res_r,
+                                       ld_resr, y_r, ld_yr, z, ld_z);
+  const GemmArgs cq = lcb_candidate_args(B_c, B_r, batch->cand2req, x_c, ld_xc, d_in_c, w_cc, b_c, d_out_c, act, z,
+                                         ld_z, res_c, ld_resc, y_c, ld_yc);
+  if (!glm_fused_supported(DType(dtype), rq, cq))
+    return fail(ROCS_ERR_UNSUPPORTED, "%s: this shape does not fit one launch (use rocs_lcb_forward)", fn);
+  const size_t need = rocs_lcb_fused_workspace_size(B_r);
+  if (!workspace || ws_bytes < need)
+    return fail(ROCS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+  ROCS_TRY(check_ptr(workspace, fn, "workspace"));
+  hipStream_t s = as_stream(stream);
+  const int n = glm_fused_flag_count(rq) + 1;
+  int* fl = static_cast<int*>(workspace);
+  ROCS_HIP(launch_pad_rows(1, 0, n, 4, nullptr, 0, fl, n, s), fn);
+  ROCS_HIP(launch_glm_fused(DType(dtype), rq, cq, fl, fl + n - 1, s), fn);
   return ok();
 }
 

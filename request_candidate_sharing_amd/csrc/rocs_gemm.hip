@@ -18,512 +18,11 @@
 // same order whichever tile shape computes it: results are bit-identical
 // across batch sizes and batch compositions.
 // Workgroup ids are remapped so that one XCD walks neighbouring tiles.
-#include "rocs_mfma.h"
+#include "rocs_gemm_tile.inc"
 
 namespace rocs {
 
 namespace {
-
-// Weight rows of the (up to four) segments.  The segment table is copied
-// out of the argument struct through an opaque asm into SGPRs and selected
-// as plain values: selected as struct fields or argument memory, the choice
-// becomes a per-lane indexed load (from argument memory, or from a private
-// copy of the table that the compiler then places in LDS).
-struct WeightSegs {
-  const bf16 *w0, *w1, *w2, *w3;
-  int e0, e1, e2;
-};
-
-__device__ __forceinline__ WeightSegs weight_segs(const GemmArgs& a) {
-  const bf16* x0 = reinterpret_cast<const bf16*>(a.W[0]);
-  const bf16* x1 = reinterpret_cast<const bf16*>(a.nseg > 1 ? a.W[1] : a.W[0]);
-  const bf16* x2 = reinterpret_cast<const bf16*>(a.nseg > 2 ? a.W[2] : a.W[0]);
-  const bf16* x3 = reinterpret_cast<const bf16*>(a.nseg > 3 ? a.W[3] : a.W[0]);
-  int y0 = a.nseg > 1 ? a.seg_end[0] : 0x7fffffff;
-  int y1 = a.nseg > 2 ? a.seg_end[1] : 0x7fffffff;
-  int y2 = a.nseg > 3 ? a.seg_end[2] : 0x7fffffff;
-  asm volatile("" : "+s"(x0), "+s"(x1), "+s"(x2), "+s"(x3), "+s"(y0), "+s"(y1), "+s"(y2));
-  return WeightSegs{x0, x1, x2, x3, y0, y1, y2};
-}
-
-__device__ __forceinline__ const bf16* weight_row(const bf16* w0, const bf16* w1, const bf16* w2, const bf16* w3,
-                                                  int e0, int e1, int e2, int64_t ldw, int n) {
-  const bf16* p = n >= e2 ? w3 : n >= e1 ? w2 : n >= e0 ? w1 : w0;
-  const int base = n >= e2 ? e2 : n >= e1 ? e1 : n >= e0 ? e0 : 0;
-  return p + int64_t(n - base) * ldw;
-}
-
-__device__ __forceinline__ const bf16* weight_row(const GemmArgs& a, int n) {
-  const WeightSegs t = weight_segs(a);
-  return weight_row(t.w0, t.w1, t.w2, t.w3, t.e0, t.e1, t.e2, a.ldw, n);
-}
-
-template <typename T>
-__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
-  return to_f(reinterpret_cast<const T*>(p)[i]);
-}
-
-// Epilogue for one output row m and four consecutive columns n..n+3:
-//   v = acc + Z[zrow(m)][n] + bias[n];  v = act(v);  v += res[m][n];  store
-// (columns >= n_split go raw to out1 instead).
-template <typename T>
-__device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const float* acc) {
-  if (m >= a.M) return;
-  int zrow = m;
-  bool bad = false;
-  if (a.z != nullptr && a.zmap != nullptr) {
-    zrow = a.zmap[m];
-    bad = (unsigned)zrow >= (unsigned)a.zrows;
-  }
-  const bool full = (n + 4 <= a.N) && (n + 4 <= a.n_split);
-  if (full) {
-    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    if (a.z != nullptr) {
-      if (bad) {
-        v[0] = v[1] = v[2] = v[3] = nan_f();
-      } else {
-        const float4 zz = *reinterpret_cast<const float4*>(a.z + int64_t(zrow) * a.ldz + n);
-        v[0] += zz.x; v[1] += zz.y; v[2] += zz.z; v[3] += zz.w;
-      }
-    }
-    if (a.bias != nullptr) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += load_elem<T>(a.bias, n + j);
-    }
-    if (a.act == 1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = fmaxf(v[j], 0.0f);
-    }
-    if (a.res != nullptr) {
-      const T* r = reinterpret_cast<const T*>(a.res) + int64_t(m) * a.ldres + n;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += to_f(r[j]);
-    }
-    if (a.out0_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out0) + int64_t(m) * a.ld0 + n) =
-          make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      T* o = reinterpret_cast<T*>(a.out0) + int64_t(m) * a.ld0 + n;
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
-        *reinterpret_cast<bf16x4*>(o) = pk;
-      } else {
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-    return;
-  }
-  for (int j = 0; j < 4; ++j) {
-    const int c = n + j;
-    if (c >= a.N) break;
-    float v = acc[j];
-    if (c < a.n_split) {
-      if (a.z != nullptr) v = bad ? nan_f() : v + a.z[int64_t(zrow) * a.ldz + c];
-      if (a.bias != nullptr) v += load_elem<T>(a.bias, c);
-      if (a.act == 1) v = fmaxf(v, 0.0f);
-      if (a.res != nullptr) v += load_elem<T>(a.res, int64_t(m) * a.ldres + c);
-      if (a.out0_f32)
-        reinterpret_cast<float*>(a.out0)[int64_t(m) * a.ld0 + c] = v;
-      else
-        reinterpret_cast<T*>(a.out0)[int64_t(m) * a.ld0 + c] = from_f<T>(v);
-    } else if (a.out1 != nullptr) {
-      a.out1[int64_t(m) * a.ld1 + (c - a.n_split)] = v;
-    }
-  }
-}
-
-// Epilogue of one element (m, c), same arithmetic as epilogue4.
-template <typename T>
-__device__ __forceinline__ void epilogue1(const GemmArgs& a, int m, int c, float v) {
-  if (m >= a.M || c >= a.N) return;
-  if (c < a.n_split) {
-    if (a.z != nullptr) {
-      const int zrow = a.zmap != nullptr ? a.zmap[m] : m;
-      v = (unsigned)zrow >= (unsigned)a.zrows ? nan_f() : v + a.z[int64_t(zrow) * a.ldz + c];
-    }
-    if (a.bias != nullptr) v += load_elem<T>(a.bias, c);
-    if (a.act == 1) v = fmaxf(v, 0.0f);
-    if (a.res != nullptr) v += load_elem<T>(a.res, int64_t(m) * a.ldres + c);
-    if (a.out0_f32)
-      reinterpret_cast<float*>(a.out0)[int64_t(m) * a.ld0 + c] = v;
-    else
-      reinterpret_cast<T*>(a.out0)[int64_t(m) * a.ld0 + c] = from_f<T>(v);
-  } else if (a.out1 != nullptr) {
-    a.out1[int64_t(m) * a.ld1 + (c - a.n_split)] = v;
-  }
-}
-
-// Per-wave LDS stage of the transposing epilogue: 32 rows of up to 64 fp32
-// accumulators (two 32x32 blocks), rows padded by 16 bytes (conflict-free
-// both ways).  Wider wave tiles go through it two blocks at a time.
-template <int FN, int JWM = 2>
-constexpr int stage_blocks() { return FN > JWM ? JWM : FN; }
-template <int FN, int JWM = 2>
-constexpr int stage_pitch() { return stage_blocks<FN, JWM>() * 32 + 4; }
-template <int FN, int JWM = 2>
-constexpr int stage_floats() { return 32 * stage_pitch<FN, JWM>(); }
-template <int FN, int JWM = 2>
-__device__ __forceinline__ int stage_at(int r, int c) { return r * stage_pitch<FN, JWM>() + c; }
-
-// Epilogue variants.  EPI_ANY tests every optional term at run time; the
-// others are fixed at compile time (request contribution gathered through
-// the map or none, bias or none, then ReLU, a residual or neither), with
-// 32-bit row offsets (launch_gemm checks the ranges).
-enum : int {
-  EPI_ANY = 0,
-  EPI_Z = 1,     // z with zmap
-  EPI_BIAS = 2,
-  EPI_RELU = 4,
-  EPI_RES = 8,
-  EPI_ZACC = 16,  // with EPI_Z: the tile's accumulators started at Z[m_i] (zinit_acc)
-  EPI_SPEC = 32,  // without EPI_Z: a fixed variant with no request contribution
-};
-
-// Writes one 32-row block-row of a wave's tile through the epilogue.  Block
-// j: lane holds row mrow0 + lane%32 and columns nb + 32j + 8g +
-// 4*(lane/32) + 0..3 in registers 4g..4g+3.  Stored directly, every
-// instruction would touch 32 rows (half the achievable write bandwidth), so
-// interior blocks pass through the wave's LDS stage and come back
-// row-contiguous (JW*8 lanes per row, 4 columns each), JW column blocks at a
-// time.  All loads of a pass (map entries, Z rows, residual) are issued
-// before its arithmetic and stores.  The arithmetic is the edge path's:
-// acc + Z + bias, act, + residual, one rounding.
-template <int FN, int EPI = EPI_ANY, int JWM = 2>
-__device__ __forceinline__ void store_row_staged(const GemmArgs& a, int mrow0, int nb, int lane,
-                                                 const f32x16 (&row)[FN], float* stage) {
-  constexpr bool ANY = EPI == EPI_ANY;
-  constexpr int JW = stage_blocks<FN, JWM>();
-  static_assert(FN % JW == 0, "column blocks must pair up");
-  constexpr int LPR = JW * 8;     // lanes per row
-  constexpr int RPI = 64 / LPR;   // rows per pass
-  constexpr int NP = 32 / RPI;    // passes per block-row
-  const int hk = lane >> 5;
-  const float* __restrict__ z = a.z;
-  const bf16* __restrict__ bias = reinterpret_cast<const bf16*>(a.bias);
-  const bf16* __restrict__ res = reinterpret_cast<const bf16*>(a.res);
-  bf16* __restrict__ out = reinterpret_cast<bf16*>(a.out0);
-  const bool has_z = ANY ? z != nullptr : (EPI & EPI_Z) != 0 && (EPI & EPI_ZACC) == 0;
-  const bool has_map = ANY ? a.zmap != nullptr : (EPI & EPI_Z) != 0 && (EPI & EPI_ZACC) == 0;
-  const bool has_bias = ANY ? bias != nullptr : (EPI & EPI_BIAS) != 0;
-  const bool relu = ANY ? a.act == 1 : (EPI & EPI_RELU) != 0;
-  const bool has_res = ANY ? res != nullptr : (EPI & EPI_RES) != 0;
-  const int rl = lane / LPR;
-#pragma unroll
-  for (int jg = 0; jg < FN / JW; ++jg) {
-    const int n = nb + jg * JW * 32 + (lane % LPR) * 4;
-    // map entries and residuals of this lane's NP rows, issued before the LDS round trip
-    int zrow[NP];
-    bf16x4 rr[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int m = min(mrow0 + p * RPI + rl, a.M - 1);
-      zrow[p] = (has_z && has_map) ? a.zmap[m] : m;
-      if (has_res) {
-        const bf16* rp = ANY ? res + int64_t(m) * a.ldres + n : res + (uint32_t(m) * uint32_t(a.ldres) + n);
-        rr[p] = *reinterpret_cast<const bf16x4*>(rp);
-      }
-    }
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (has_bias) {
-      const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + n);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = to_f(bb[e]);
-    }
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& c = row[jg * JW + jj];
-        *reinterpret_cast<f32x4*>(stage + stage_at<FN, JWM>(lane & 31, jj * 32 + 8 * g + 4 * hk)) =
-            f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
-      }
-    __builtin_amdgcn_wave_barrier();
-    float4 zz[NP];
-    bool bad[NP];
-    if (has_z) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        bad[p] = (unsigned)zrow[p] >= (unsigned)a.zrows;
-        const int zr = bad[p] ? 0 : zrow[p];
-        const float* zp = ANY ? z + int64_t(zr) * a.ldz + n : z + (uint32_t(zr) * uint32_t(a.ldz) + n);
-        zz[p] = *reinterpret_cast<const float4*>(zp);
-      }
-    }
-    f32x4 sv[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      sv[p] = *reinterpret_cast<const f32x4*>(stage + stage_at<FN, JWM>(p * RPI + rl, (lane % LPR) * 4));
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int m = mrow0 + p * RPI + rl;
-      float v[4] = {sv[p][0], sv[p][1], sv[p][2], sv[p][3]};
-      if (has_z) {
-        v[0] = bad[p] ? nan_f() : v[0] + zz[p].x;
-        v[1] = bad[p] ? nan_f() : v[1] + zz[p].y;
-        v[2] = bad[p] ? nan_f() : v[2] + zz[p].z;
-        v[3] = bad[p] ? nan_f() : v[3] + zz[p].w;
-      }
-      if (has_bias)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += bv[e];
-      if (relu)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
-      if (has_res)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += to_f(rr[p][e]);
-      if (m < a.M) {
-        bf16x4 pk = {to_bf(v[0]), to_bf(v[1]), to_bf(v[2]), to_bf(v[3])};
-        bf16* op = ANY ? out + int64_t(m) * a.ld0 + n : out + (uint32_t(m) * uint32_t(a.ld0) + n);
-        *reinterpret_cast<bf16x4*>(op) = pk;
-      }
-    }
-  }
-}
-
-// Edge block-rows (N tail, the split between the two outputs, fp32 output):
-// the block-row goes through the LDS stage too, then one element per lane
-// at a time through epilogue1 (no register array is indexed at run time).
-template <int FN, int JWM = 2>
-__device__ __forceinline__ void store_row_edge(const GemmArgs& a, int mrow0, int nb, int lane,
-                                               const f32x16 (&row)[FN], float* stage) {
-  constexpr int JW = stage_blocks<FN, JWM>();
-  constexpr int W = JW * 32;
-  const int hk = lane >> 5;
-#pragma unroll
-  for (int jg = 0; jg < FN / JW; ++jg) {
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& c = row[jg * JW + jj];
-        *reinterpret_cast<f32x4*>(stage + stage_at<FN, JWM>(lane & 31, jj * 32 + 8 * g + 4 * hk)) =
-            f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
-      }
-    __builtin_amdgcn_wave_barrier();
-    for (int e = lane; e < 32 * W; e += 64) {
-      const int r = e / W, c = e % W;
-      epilogue1<bf16>(a, mrow0 + r, nb + jg * W + c, stage[stage_at<FN, JWM>(r, c)]);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-template <int FN, int EPI, int JWM>
-__device__ __forceinline__ void store_row(const GemmArgs& a, int mrow0, int nb, int lane, const f32x16 (&row)[FN],
-                                          float* stage) {
-  const bool interior = (nb + FN * 32 <= a.N) && (nb + FN * 32 <= a.n_split) && !a.out0_f32;
-  if (interior)
-    store_row_staged<FN, EPI, JWM>(a, mrow0, nb, lane, row, stage);
-  else
-    store_row_edge<FN, JWM>(a, mrow0, nb, lane, row, stage);
-}
-
-template <int EPI, int JWM, int FM, int FN>
-__device__ __forceinline__ void store_blocks_as(const GemmArgs& a, int mb, int nb, int lane,
-                                                const f32x16 (&acc)[FM][FN], float* stage) {
-#pragma unroll
-  for (int i = 0; i < FM; ++i) store_row<FN, EPI, JWM>(a, mb + i * 32, nb, lane, acc[i], stage);
-}
-
-// The epilogue variant is uniform per launch: one switch, then straight-line
-// code without per-element feature tests.
-template <int JWM = 2, int FM, int FN>
-__device__ __forceinline__ void store_blocks(const GemmArgs& a, int mb, int nb, int lane, const f32x16 (&acc)[FM][FN],
-                                             float* stage) {
-#define ROCS_EPI_CASE(V) \
-  case (V): store_blocks_as<(V), JWM>(a, mb, nb, lane, acc, stage); break;
-#define ROCS_EPI_TAILS(P) \
-  ROCS_EPI_CASE(P) ROCS_EPI_CASE(P | EPI_RELU) ROCS_EPI_CASE(P | EPI_RES) ROCS_EPI_CASE(P | EPI_BIAS) \
-  ROCS_EPI_CASE(P | EPI_BIAS | EPI_RELU) ROCS_EPI_CASE(P | EPI_BIAS | EPI_RES)
-  switch (a.epi) {
-    ROCS_EPI_TAILS(EPI_Z)
-    ROCS_EPI_TAILS(EPI_Z | EPI_ZACC)
-    ROCS_EPI_TAILS(EPI_SPEC)
-    default: store_blocks_as<EPI_ANY, JWM>(a, mb, nb, lane, acc, stage); break;
-  }
-#undef ROCS_EPI_TAILS
-#undef ROCS_EPI_CASE
-}
-
-// ----------------------------------------------------------------- DMA-staged bf16 GEMM
-// For the candidate-batch GEMMs (M = B_c in the tens of thousands).  A
-// BM x BN tile per workgroup of WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 blocks.  Operand slabs (64 wide in K)
-// move global -> LDS with global_load_lds_dwordx4 (no register staging)
-// through a ring of NS slab buffers: NS-1 slabs are in flight while one is
-// multiplied, which hides the HBM latency of the activation rows (each slab
-// of a 512-deep K is a fresh HBM read).  Each wave-instruction fills 1 KB of
-// LDS (8 rows of 128 B); lane i fetches the global chunk that the row
-// swizzle places at its LDS slot.  Chunks past K come from a zero page, so K
-// tails need no masking (K is a multiple of 8: weight and activation rows
-// are 16-byte aligned).
-__device__ uint4 g_zero_page[4];
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt with vmcnt(N), expcnt and lgkmcnt left at their maxima (gfx9
-// encoding: vmcnt bits [3:0] and [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Wait until at most `newer` slabs of PER instructions each are outstanding
-// (0 <= newer <= MAXN; the immediate must be a compile-time constant).
-template <int PER, int MAXN>
-__device__ __forceinline__ void wait_slabs(int newer) {
-  if constexpr (MAXN > 0) {
-    if (newer >= MAXN) {
-      wait_vmcnt<PER * MAXN>();
-      return;
-    }
-    wait_slabs<PER, MAXN - 1>(newer);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-// This wave's share of the slab DMA for one BM x BN tile: PER
-// wave-instructions per 64-wide slab, each filling 1 KB of the ring (8 rows
-// of 128 B); lane i fetches the global chunk that the row swizzle places at
-// its LDS slot.  Chunks past K come from the zero page.
-template <int BM, int BN, int NW>
-struct SlabFeed {
-  static constexpr int CPR = 8, RPI = 8;
-  static constexpr int RB = (BM + BN) / RPI;
-  static_assert(RB % NW == 0, "row blocks must divide among waves");
-  static constexpr int PER = RB / NW;
-  const bf16* src[PER];
-  int kofs[PER];
-  __device__ __forceinline__ void init(const GemmArgs& a, const WeightSegs& ws, int m0, int n0, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int r = (wave * PER + j) * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ swz<CPR>(r);
-      kofs[j] = chunk * 8;
-      if (r < BM)
-        src[j] = reinterpret_cast<const bf16*>(a.A) + int64_t(min(m0 + r, a.M - 1)) * a.lda + chunk * 8;
-      else
-        src[j] = weight_row(ws.w0, ws.w1, ws.w2, ws.w3, ws.e0, ws.e1, ws.e2, a.ldw, min(n0 + r - BM, a.N - 1)) +
-                 chunk * 8;
-    }
-  }
-  __device__ __forceinline__ void issue(int K, const void* zero, int k0, uint4* slot, int wave) const {
-    if (k0 + CPR * 8 <= K) {  // a whole slab inside K (a wave-uniform branch): no per-lane select
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)(slot + (wave * PER + j) * 64), 16, 0, 0);
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const void* p = (k0 + kofs[j] < K) ? static_cast<const void*>(src[j] + k0) : zero;
-      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(slot + (wave * PER + j) * 64), 16, 0, 0);
-    }
-  }
-};
-
-// The zero page's address comes from the GOT.  Loaded inside a loop, that
-// scalar load (out of order with LDS reads on the same counter) would turn
-// every fragment wait into a full lgkmcnt(0); pinned in SGPRs by the caller,
-// it is loaded once.
-__device__ __forceinline__ const void* pinned_zero_page() {
-  const void* zero = g_zero_page;
-  asm volatile("" : "+s"(zero));
-  return zero;
-}
-
-// Starts a wave's accumulators at the request contribution Z[m_i] of its
-// rows (EPI_ZACC launches), so the epilogue has nothing left to gather and
-// the Z loads overlap the first slab's DMA: acc = Z[m] + the products, in
-// that order.  A row whose map entry is out of range starts at NaN.  Block
-// (i, j): lane holds row mb + 32i + lane%32 and columns nb + 32j + 8g +
-// 4*(lane/32) + 0..3 in registers 4g..4g+3.  Offsets are 32-bit (checked
-// when the variant is chosen).
-template <int FM, int FN>
-__device__ __forceinline__ void zinit_acc(const GemmArgs& a, int mb, int nb, int lane, f32x16 (&acc)[FM][FN]) {
-  const int hk = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = min(mb + i * 32 + (lane & 31), a.M - 1);
-    const int zr = a.zmap ? a.zmap[row] : row;  // no map: Z has one row per output row
-    const bool bad = (unsigned)zr >= (unsigned)a.zrows;
-    const float* zp = a.z + (uint32_t(bad ? 0 : zr) * uint32_t(a.ldz) + uint32_t(nb + 4 * hk));
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(zp + j * 32 + 8 * g);
-        acc[i][j][4 * g + 0] = bad ? nan_f() : v.x;
-        acc[i][j][4 * g + 1] = bad ? nan_f() : v.y;
-        acc[i][j][4 * g + 2] = bad ? nan_f() : v.z;
-        acc[i][j][4 * g + 3] = bad ? nan_f() : v.w;
-      }
-  }
-}
-
-// One BM x BN output tile at (m0, n0) on a workgroup of WM x WN waves, with
-// the ring (NS slots of BM + BN rows of one 64-wide slab) at smem; slab kb
-// lives in slot kb % NS.
-template <int BM, int BN, int WM, int WN, int NS>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int m0, int n0, uint4* smem) {
-  constexpr int BK = 64;
-  constexpr int NW = WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int CPR = BK / 8;
-  constexpr int SLOT = (BM + BN) * CPR;
-  static_assert(NW * stage_floats<FN>() * 4 <= NS * SLOT * 16, "epilogue stage exceeds the ring");
-  using Feed = SlabFeed<BM, BN, NW>;
-  static_assert(NS >= 2 && Feed::PER * (NS - 2) < 64, "ring depth");
-  // the wave index is uniform: the LDS slot addresses of the DMA stay scalar
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const void* zero = pinned_zero_page();
-  const WeightSegs ws = weight_segs(a);
-  auto slot = [&](int kb) { return smem + (kb % NS) * SLOT; };
-
-  Feed feed;
-  feed.init(a, ws, m0, n0, wave, lane);
-  f32x16 acc[FM][FN];
-
-  const int nk = (a.K + BK - 1) / BK;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) feed.issue(a.K, zero, s * BK, slot(s), wave);
-  if (a.epi & EPI_ZACC)
-    zinit_acc(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
-  else
-    zero_acc(acc);
-
-  const int xr0 = wm * WTM + (lane & 31);
-  const int wr0 = BM + wn * WTN + (lane & 31);
-  Frags<FM, FN> fr;
-  for (int kb = 0; kb < nk - 1; ++kb) {
-    // Slab kb has landed once at most min(NS-2, nk-1-kb) newer slabs (PER
-    // instructions each, returned in order) are still outstanding.
-    wait_slabs<Feed::PER, NS - 2>(min(NS - 2, nk - 1 - kb));
-    // every wave's part of slab kb is in LDS, and every wave is done with
-    // slab kb-1 (its last step's fragments are in registers), whose slot
-    // the next issue refills
-    __syncthreads();
-    if (kb + NS - 1 < nk) feed.issue(a.K, zero, (kb + NS - 1) * BK, slot(kb + NS - 1), wave);
-    const uint4* sl = slot(kb);
-    mfma_slab_carry<FM, FN, CPR, CPR>(fr, kb > 0, sl, wr0, sl, xr0, lane >> 5, acc);
-  }
-  if (nk > 0) {  // the last slab, then the carried step
-    wait_vmcnt<0>();
-    __syncthreads();
-    const uint4* sl = slot(nk - 1);
-    mfma_slab_carry<FM, FN, CPR, CPR>(fr, nk > 1, sl, wr0, sl, xr0, lane >> 5, acc);
-    mfma_frags(fr, 1, acc);
-  }
-  __syncthreads();  // every wave is done reading the ring: the epilogue stages in it
-  store_blocks(a, m0 + wm * WTM, n0 + wn * WTN, lane, acc, reinterpret_cast<float*>(smem) + wave * stage_floats<FN>());
-}
 
 // One tile per workgroup, tiles in XCD-aware order.  A batch of GEMMs is
 // one flat grid of (GEMM, tile) pairs, remapped as a whole, so each XCD
@@ -564,69 +63,20 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_mixed_kernel(GemmArgs a, int
 
 // Launches of fewer than 2,048 rows with a long K (K >= 1024; few output
 // tiles, each a long chain of slabs), and request-side launches with fewer
-// 32 x 32 tiles than CUs: 32 x 32 output tiles, four waves per tile, wave w reducing the
-// contiguous K quarter [w nk / 4, (w + 1) nk / 4) through a ring of its own
-// (no workgroup barrier in the loop).  The four fp32 partial tiles are then
-// added in a fixed order, ((p0 + p1) + p2) + p3, and wave 0 runs the
-// epilogue.  The result is deterministic; it is summed in a different order
-// than the single-chain kernels.  The choice depends on the launch's shape
-// only (uses_splitk).
+// 32 x 32 tiles than CUs: one 32 x 32 tile per workgroup of four waves, K
+// split in quarters (splitk_tile).  The result is deterministic; it is summed
+// in a different order than the single-chain kernels.  The choice depends on
+// the launch's shape only (uses_splitk).
 template <int NS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_splitk_kernel(GemmArgs a0) {
   const GemmArgs a = batch_slice(a0, blockIdx.y);  // GEMM blockIdx.y of a batch
-  constexpr int BM = 32, BN = 32, BK = 64, CPR = 8, SLOT = (BM + BN) * CPR, SPLIT = 4;
-  __shared__ uint4 smem[SPLIT * NS * SLOT];
-  using Feed = SlabFeed<BM, BN, 1>;
-  static_assert(Feed::PER * (NS - 2) < 64, "ring depth");
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = (a.M + BM - 1) / BM;
+  constexpr int SLOT = (32 + 32) * 8;
+  __shared__ uint4 smem[4 * NS * SLOT];
+  const int ntn = (a.N + 31) / 32;
+  const int ntm = (a.M + 31) / 32;
   const int logical = xcd_remap(blockIdx.x, ntm * ntn);
-  const int m0 = (logical / ntn) * BM, n0 = (logical % ntn) * BN;
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const void* zero = pinned_zero_page();
-  const WeightSegs ws = weight_segs(a);
-  uint4* ring = smem + wave * NS * SLOT;
-  auto slot = [&](int i) { return ring + (i % NS) * SLOT; };
-
-  const int nk = (a.K + BK - 1) / BK;
-  const int k_lo = (wave * nk) / SPLIT, k_hi = ((wave + 1) * nk) / SPLIT;
-  const int n = k_hi - k_lo;  // slabs of this wave
-  Feed feed;
-  feed.init(a, ws, m0, n0, 0, lane);
-  f32x16 acc[1][1];
-  zero_acc(acc);
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (i < n) feed.issue(a.K, zero, (k_lo + i) * BK, slot(i), 0);
-  Frags<1, 1> fr;
-  for (int i = 0; i < n; ++i) {
-    wait_slabs<Feed::PER, NS - 2>(min(NS - 2, n - 1 - i));
-    __builtin_amdgcn_wave_barrier();
-    if (i + NS - 1 < n) feed.issue(a.K, zero, (k_lo + i + NS - 1) * BK, slot(i + NS - 1), 0);
-    const uint4* sl = slot(i);
-    mfma_slab_carry<1, 1, CPR, CPR>(fr, i > 0, sl, BM + (lane & 31), sl, lane & 31, lane >> 5, acc);
-  }
-  if (n > 0) mfma_frags(fr, 1, acc);
-  __syncthreads();  // every wave is done with its ring: the partials go there
-  float* part = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) part[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float v = part[r * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < SPLIT; ++w) v += part[(w * 16 + r) * 64 + lane];
-    acc[0][0][r] = v;
-  }
-  // The partial sums started at zero, so the epilogue adds Z: the mapped
-  // variant without EPI_ZACC, or the generic one when Z has no map (only
-  // EPI_ZACC variants accept an unmapped Z).
-  GemmArgs e = a;
-  if (e.epi & EPI_ZACC) e.epi = a.zmap ? (e.epi & ~EPI_ZACC) : EPI_ANY;
-  store_blocks(e, m0, n0, lane, acc, part + SPLIT * 16 * 64);
+  splitk_tile<NS>(a, (logical / ntn) * 32, (logical % ntn) * 32, smem, wave, threadIdx.x & 63, true);
 }
 
 // fp32 path: LDS-tiled SIMT GEMM, 64 x 64 tile, each thread 4 x 4 outputs,
@@ -705,11 +155,6 @@ int device_cus() {
 // tiles) takes 256-row tiles for 4 rounds and a round of 128-row tiles
 // (116 vs 121 us for 256 rows throughout); N = 512 takes 192-row tiles
 // (109 vs 111 us mixed, 125 us with 256 rows).
-struct CandPlan {
-  int h;             // uniform tile height, or 0 for the mixed plan
-  int M1, h2, grid;  // mixed plan
-};
-
 CandPlan cand_plan(int M, int ntn) {
   const int cus = device_cus();
   const auto tile_cost = [](int h) { return 0.52 + 0.48 * h / 256.0; };

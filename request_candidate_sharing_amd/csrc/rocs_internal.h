@@ -69,6 +69,26 @@ __host__ __device__ inline GemmArgs batch_slice(const GemmArgs& a, int i) {
 }
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
+// Launch choices of launch_gemm, by shape: the epilogue variant, whether a
+// launch of fewer than 2,048 rows splits K, and the candidate tile plan.
+int epilogue_variant(const GemmArgs& a);
+bool uses_splitk(const GemmArgs& a);
+struct CandPlan {
+  int h;             // uniform tile height, or 0 for the mixed plan
+  int M1, h2, grid;  // mixed plan: rows [0, M1) in 256-row tiles, then h2-row tiles
+};
+CandPlan cand_plan(int M, int ntn);
+// One launch for both halves of a GLM linear: the request tiles ([Y_R | Z])
+// and the candidate tiles, which wait for the request rows they read on
+// completion counters instead of a kernel boundary.  `flags` holds
+// glm_fused_flag_count(req) zeroed ints (left nonzero: zero them again
+// before the next launch), `err` one int set to 1 if a wait gave up.  Returns
+// hipErrorNotSupported, having launched nothing, when the pair does not fit
+// (glm_fused_supported).
+bool glm_fused_supported(DType dt, const GemmArgs& req, const GemmArgs& cand);
+int glm_fused_flag_count(const GemmArgs& req);
+hipError_t launch_glm_fused(DType dt, const GemmArgs& req, const GemmArgs& cand, int* flags, int* err,
+                            hipStream_t s);
 // Whether launch_gemm sums this launch as Z + products (accumulators started
 // at the gathered Z rows) rather than products + Z.
 bool gemm_z_in_accumulators(const GemmArgs& a);

@@ -28,7 +28,7 @@ ROCS_ERR_UNSUPPORTED = -8
 ROCS_F32, ROCS_BF16 = 0, 1
 ROCS_ACT_NONE, ROCS_ACT_RELU = 0, 1
 ROCS_NORM_LAYER, ROCS_NORM_RMS = 0, 1
-ROCS_EXEC_SHARED, ROCS_EXEC_DENSE_BROADCAST, ROCS_EXEC_SHARED_SERIAL = 0, 1, 2
+ROCS_EXEC_SHARED, ROCS_EXEC_DENSE_BROADCAST, ROCS_EXEC_SHARED_SERIAL, ROCS_EXEC_SHARED_FUSED = 0, 1, 2, 3
 ROCS_OP_LINEAR, ROCS_OP_NORM, ROCS_OP_FM, ROCS_OP_TOKEN_LCB, ROCS_OP_XATTN, ROCS_OP_HEAD = 1, 2, 3, 4, 5, 6
 
 c_int32, c_int64, c_size_t, c_float, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
@@ -132,6 +132,9 @@ _SIGS = {
                            c_int64, P],
     "rocs_lcb_forward": [P, c_int32, P, c_int64, c_int32, P, c_int64, c_int32, P, P, P, P, P, c_int32, c_int32,
                          c_int32, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P],
+    "rocs_lcb_fused_workspace_size": [c_int32],
+    "rocs_lcb_forward_fused": [P, c_int32, P, c_int64, c_int32, P, c_int64, c_int32, P, P, P, P, P, c_int32, c_int32,
+                               c_int32, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P, c_int64, P, c_size_t, P],
     "rocs_head_forward": [P, c_int32, P, c_int64, c_int32, P, c_int64, c_int32, P, P, c_float, P, P, P],
     "rocs_group_norm": [c_int32, c_int32, c_float, c_int32, c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, P,
                         P, P, P, P, c_int32, P, c_int64, P, c_int64, P],
@@ -164,6 +167,7 @@ _SIGS = {
     "rocs_version": [],
 }
 _RES = {
+    "rocs_lcb_fused_workspace_size": c_size_t,
     "rocs_dca_encode_kv_workspace_size": c_size_t,
     "rocs_dca_cross_attn_workspace_size": c_size_t,
     "rocs_dca_request_attn_workspace_size": c_size_t,
@@ -253,6 +257,20 @@ def rocs_lcb_forward(batch_, dtype, x_r, ld_xr, d_in_r, x_c, ld_xc, d_in_c, w_rr
     st = lib().rocs_lcb_forward(_b(batch_), dtype, ptr(x_r), ld_xr, d_in_r, ptr(x_c), ld_xc, d_in_c, ptr(w_rr),
                                 ptr(w_cr), ptr(w_cc), ptr(b_r), ptr(b_c), d_out_r, d_out_c, act, ptr(res_r), ld_resr,
                                 ptr(res_c), ld_resc, ptr(y_r), ld_yr, ptr(y_c), ld_yc, ptr(z), ld_z, stream)
+    return _check(st) if check else st
+
+
+def rocs_lcb_fused_workspace_size(B_r) -> int:
+    return int(lib().rocs_lcb_fused_workspace_size(B_r))
+
+
+def rocs_lcb_forward_fused(batch_, dtype, x_r, ld_xr, d_in_r, x_c, ld_xc, d_in_c, w_rr, w_cr, w_cc, b_r, b_c,
+                           d_out_r, d_out_c, act, res_r, ld_resr, res_c, ld_resc, y_r, ld_yr, y_c, ld_yc, z, ld_z,
+                           workspace, ws_bytes, stream=None, check=True):
+    st = lib().rocs_lcb_forward_fused(_b(batch_), dtype, ptr(x_r), ld_xr, d_in_r, ptr(x_c), ld_xc, d_in_c,
+                                      ptr(w_rr), ptr(w_cr), ptr(w_cc), ptr(b_r), ptr(b_c), d_out_r, d_out_c, act,
+                                      ptr(res_r), ld_resr, ptr(res_c), ld_resc, ptr(y_r), ld_yr, ptr(y_c), ld_yc,
+                                      ptr(z), ld_z, ptr(workspace), ws_bytes, stream)
     return _check(st) if check else st
 
 

@@ -346,3 +346,30 @@ def test_stack_accepts_ragged_widths():
     st = R.rocs_lcb_request(R.ROCS_BF16, 4, FAKE, 40, 37, FAKE, FAKE, None, 33, 33, 0, None, 0, FAKE, 40, FAKE, 40,
                             check=False)
     assert st == R.ROCS_ERR_ALIGN
+
+
+def _lcb_fused(**kw):
+    a = dict(batch_=R.batch(4, 4096, None, FAKE), dtype=R.ROCS_BF16, x_r=FAKE, ld_xr=512, d_in_r=512, x_c=FAKE,
+             ld_xc=512, d_in_c=512, w_rr=FAKE, w_cr=FAKE, w_cc=FAKE, b_r=None, b_c=None, d_out_r=1024,
+             d_out_c=1024, act=R.ROCS_ACT_RELU, res_r=None, ld_resr=0, res_c=None, ld_resc=0, y_r=FAKE, ld_yr=1024,
+             y_c=FAKE, ld_yc=1024, z=FAKE, ld_z=1024, workspace=FAKE,
+             ws_bytes=R.rocs_lcb_fused_workspace_size(4))
+    a.update(kw)
+    return R.rocs_lcb_forward_fused(**a, stream=None, check=False)
+
+
+def test_lcb_fused_host_checks():
+    """The one-launch GLM linear: shapes that do not fit one grid are
+    rejected before anything is enqueued, and so is a short workspace (one
+    completion counter per 32 request rows, plus an error word)."""
+    assert R.rocs_lcb_fused_workspace_size(4) >= 8
+    assert R.rocs_lcb_fused_workspace_size(4000) >= (4000 + 31) // 32 * 4 + 4
+    assert _lcb_fused(batch_=R.batch(4, 1000, None, FAKE)) == R.ROCS_ERR_UNSUPPORTED  # B_c < 2048
+    assert _lcb_fused(batch_=R.batch(2048, 4096, None, FAKE)) == R.ROCS_ERR_UNSUPPORTED  # B_r >= 2048
+    assert _lcb_fused(d_out_c=384, ld_yc=384, ld_z=384) == R.ROCS_ERR_UNSUPPORTED  # not a multiple of 256
+    assert _lcb_fused(dtype=R.ROCS_F32) == R.ROCS_ERR_UNSUPPORTED
+    assert _lcb_fused(res_c=FAKE, ld_resc=1024) == R.ROCS_ERR_UNSUPPORTED  # ReLU and a residual
+    assert _lcb_fused(ws_bytes=4) == R.ROCS_ERR_WORKSPACE
+    assert _lcb_fused(workspace=None) == R.ROCS_ERR_WORKSPACE
+    assert _lcb_fused(x_r=None) == R.ROCS_ERR_INVALID_ARG
+    assert _lcb_fused(x_c=FAKE + 2) == R.ROCS_ERR_ALIGN

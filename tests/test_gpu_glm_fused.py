@@ -1,0 +1,225 @@
+"""The GLM linear as one launch (request and candidate tiles in one grid,
+completion counters instead of a kernel boundary) against the two-launch
+path and the oracle.
+
+rocs_lcb_forward_fused must give the bits of rocs_lcb_forward on the same
+inputs: its request tiles follow the request launch's K order (one chain,
+or four K quarters where the request launch splits K) and its candidate
+tiles the candidate launch's (accumulators started at Z).  Floating-point
+parity with the oracle uses max|gpu - oracle| / max|oracle| <= 2e-2 (bf16).
+"""
+
+import numpy as np
+import pytest
+
+import rocs_synth as S
+from oracle import ops
+from gpu_util import TOL_BF16, dev, rand, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _R():
+    from request_candidate_sharing_amd import rocs as R
+
+    return R
+
+
+def _padded(rows, width, ld, dtype=torch.bfloat16):
+    st = torch.full((max(rows, 1), ld), float("nan"), dtype=dtype, device="cuda")
+    return st[:rows, :width]
+
+
+def _put(a, ld, dtype=torch.bfloat16):
+    v = _padded(a.shape[0], a.shape[1], ld, dtype)
+    if a.shape[0]:
+        v.copy_(torch.as_tensor(np.asarray(a, np.float32), device="cuda").to(dtype))
+    return v
+
+
+class Case:
+    """Seeded bf16 inputs of one GLM linear, its outputs for both paths."""
+
+    def __init__(self, counts, d_in_r, d_in_c, d_out_r, d_out_c, act, seed, res=False, bias=True, shuffle=False):
+        R = _R()
+        rng = np.random.default_rng(seed)
+        bt = S.make_batch(counts)
+        self.B, self.Bc = len(counts), int(np.sum(counts))
+        self.dims = (d_in_r, d_in_c, d_out_r, d_out_c)
+        self.act, self.has_res = act, res
+        m = np.asarray(bt["cand2req"], np.int32)
+        perm = rng.permutation(self.Bc) if shuffle else np.arange(self.Bc)
+        self.m = m[perm]
+        self.x_r = rand(rng, (self.B, d_in_r), True)
+        self.W = rand(rng, (d_out_r + d_out_c, d_in_r + d_in_c), True, (d_in_r + d_in_c) ** -0.5)
+        self.b = rand(rng, d_out_r + d_out_c, True, 0.5) if bias else np.zeros(d_out_r + d_out_c, np.float32)
+        self.r_r = rand(rng, (self.B, d_out_r), True)
+        self.x_c = rand(rng, (self.Bc, d_in_c), True)
+        self.r_c = rand(rng, (self.Bc, d_out_c), True)
+        ld = lambda w: w + 8
+        self.t = dict(
+            x_r=_put(self.x_r, ld(d_in_r)), x_c=_put(self.x_c, ld(d_in_c)),
+            w_rr=dev(self.W[:d_out_r, :d_in_r], torch.bfloat16), w_cr=dev(self.W[d_out_r:, :d_in_r], torch.bfloat16),
+            w_cc=dev(self.W[d_out_r:, d_in_r:], torch.bfloat16),
+            b_r=dev(self.b[:d_out_r], torch.bfloat16) if bias and d_out_r else None,
+            b_c=dev(self.b[d_out_r:], torch.bfloat16) if bias else None,
+            r_r=_put(self.r_r, ld(d_out_r)) if res and d_out_r else None,
+            r_c=_put(self.r_c, ld(d_out_c)) if res else None)
+        off = torch.as_tensor(bt["offsets"], device="cuda") if not shuffle else None
+        self.c2r = torch.as_tensor(self.m, device="cuda")
+        self.batch = R.batch(self.B, self.Bc, off, self.c2r)
+        self.ws = torch.empty(R.rocs_lcb_fused_workspace_size(self.B), dtype=torch.uint8, device="cuda")
+        self.ws.fill_(0xA5)  # arbitrary contents: the call zeroes its counters itself
+
+    def outputs(self):
+        d_in_r, d_in_c, d_out_r, d_out_c = self.dims
+        return (_padded(self.B, d_out_r, d_out_r + 8), _padded(self.Bc, d_out_c, d_out_c + 8),
+                _padded(self.B, d_out_c, d_out_c + 4, torch.float32))
+
+    def run(self, fused, outs=None, stream=None, check=True):
+        R = _R()
+        d_in_r, d_in_c, d_out_r, d_out_c = self.dims
+        t = self.t
+        y_r, y_c, z = outs if outs is not None else self.outputs()
+        args = (self.batch, R.ROCS_BF16, t["x_r"], t["x_r"].stride(0), d_in_r, t["x_c"], t["x_c"].stride(0), d_in_c,
+                t["w_rr"], t["w_cr"], t["w_cc"], t["b_r"], t["b_c"], d_out_r, d_out_c, self.act, t["r_r"],
+                t["r_r"].stride(0) if t["r_r"] is not None else 0, t["r_c"],
+                t["r_c"].stride(0) if t["r_c"] is not None else 0, y_r, y_r.stride(0), y_c, y_c.stride(0), z,
+                z.stride(0))
+        s = stream if stream is not None else R.cur_stream()
+        if fused:
+            st = R.rocs_lcb_forward_fused(*args, self.ws, self.ws.numel(), s, check=check)
+        else:
+            st = R.rocs_lcb_forward(*args, s, check=check)
+        return st, (y_r, y_c, z)
+
+    def both(self):
+        _, a = self.run(False)
+        _, b = self.run(True)
+        torch.cuda.synchronize()
+        return [to_np(x) for x in a], [to_np(x) for x in b]
+
+    def oracle(self, rows):
+        """Oracle outputs of candidate rows `rows` and every request row."""
+        d_in_r, d_in_c, d_out_r, d_out_c = self.dims
+        dense_c = np.concatenate([self.x_r[self.m[rows]], self.x_c[rows]], 1)
+        dense_r = np.concatenate([self.x_r, np.zeros((self.B, d_in_c), np.float32)], 1)
+        yc = ops.glm_linear(dense_c, self.W, self.b, d_in_r, d_out_r)[:, d_out_r:]
+        yr = ops.glm_linear(dense_r, self.W, self.b, d_in_r, d_out_r)[:, :d_out_r]
+        if self.act == _R().ROCS_ACT_RELU:
+            yc, yr = ops.relu(yc), ops.relu(yr)
+        if self.has_res:
+            yc = yc + self.r_c[rows]
+            yr = yr + self.r_r
+        return yr, yc
+
+
+def _counts(rng, n_req, mean, lo=0):
+    return list(rng.integers(lo, 2 * mean, n_req))
+
+
+CASES = [
+    # request tiles in one K chain (200 request rows: a ragged 64-row tile), mixed candidate plan
+    dict(counts=("r", 200, 26), dims=(512, 512, 512, 1024), act=1, seed=31),
+    # request launch splits K (K = 1096: a slab tail), residual + bias, no activation
+    dict(counts=("r", 40, 80), dims=(1096, 1024, 128, 512), act=0, seed=32, res=True),
+    # request rows only feed Z (d_out_r = 0), 256-wide output
+    dict(counts=("r", 70, 45), dims=(256, 384, 0, 256), act=1, seed=33),
+    # arbitrary candidate order: a tile's map entries span many request blocks
+    dict(counts=("r", 200, 26), dims=(512, 512, 512, 1024), act=1, seed=34, shuffle=True),
+    # one request, many candidates; empty-request neighbours
+    dict(counts=[0, 2600, 0], dims=(64, 128, 64, 512), act=1, seed=35),
+]
+
+
+def _make(c):
+    counts = c["counts"]
+    if counts[0] == "r":
+        counts = _counts(np.random.default_rng(c["seed"]), counts[1], counts[2])
+    return Case(counts, *c["dims"], c["act"], c["seed"], res=c.get("res", False), shuffle=c.get("shuffle", False))
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_fused_glm_bit_identical_to_two_launches(ci):
+    c = _make(CASES[ci])
+    assert c.Bc >= 2048
+    two, one = c.both()
+    for name, a, b in zip(("y_r", "y_c", "z"), two, one):
+        if a.size:
+            assert np.array_equal(a, b, equal_nan=True), name
+    assert np.isfinite(one[1]).all()
+
+
+@pytest.mark.parametrize("ci", [0, 1, 3])
+def test_fused_glm_matches_oracle(ci):
+    c = _make(CASES[ci])
+    _, (y_r, y_c, z) = c.run(True)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(c.Bc, 300, replace=False)
+    yr, yc = c.oracle(rows)
+    assert rel_err(to_np(y_c)[rows], yc) <= TOL_BF16
+    if c.dims[2]:
+        assert rel_err(to_np(y_r), yr) <= TOL_BF16
+
+
+def test_fused_glm_calls_in_a_row_and_smaller_batch():
+    """The counters are zeroed by every call: a second call on the same
+    workspace (and a third with fewer requests and candidates) equals the
+    two-launch path."""
+    big = _make(CASES[0])
+    small = Case(_counts(np.random.default_rng(9), 90, 40, lo=1), 512, 512, 512, 1024, 1, seed=36)
+    small.ws = big.ws  # shared workspace, larger than the small batch needs
+    for c in (big, big, small):
+        two, one = c.both()
+        for a, b in zip(two, one):
+            assert np.array_equal(a, b, equal_nan=True)
+
+
+def test_fused_glm_replays_from_a_graph():
+    """Captured (the counter reset is a kernel, not a memset), every replay
+    equals the eager call, with other work between replays."""
+    c = _make(CASES[1])
+    other = _make(CASES[2])
+    outs = c.outputs()
+    c.run(True, outs)
+    torch.cuda.synchronize()
+    eager = [to_np(x) for x in outs]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        c.run(True, outs, stream=s.cuda_stream)
+    for i in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        g.replay()
+        other.both()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, outs):
+            assert np.array_equal(a, to_np(b), equal_nan=True), i
+
+
+def test_fused_glm_rejects_shapes_that_do_not_fit():
+    R = _R()
+    c = Case([5, 900], 64, 64, 64, 256, 1, seed=37)  # B_c < 2048
+    st, _ = c.run(True, check=False)
+    assert st == R.ROCS_ERR_UNSUPPORTED
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["up", "down"])
+def test_fused_glm_full_size_glm_mlp_shapes(layer):
+    """The GLM MLP stack's linears at full size (256 requests, 73,704
+    candidates): 512 -> 1024 with ReLU (request tiles in one K chain) and
+    1024 -> 512 with a residual (request launch splits K)."""
+    counts = _counts(np.random.default_rng(102), 256, 288)
+    dims = (512, 512, 1024, 1024) if layer == "up" else (1024, 1024, 512, 512)
+    c = Case(counts, *dims, 1 if layer == "up" else 0, seed=38, res=layer == "down")
+    two, one = c.both()
+    for name, a, b in zip(("y_r", "y_c", "z"), two, one):
+        assert np.array_equal(a, b, equal_nan=True), name
+    rows = np.random.default_rng(6).choice(c.Bc, 200, replace=False)
+    yr, yc = c.oracle(rows)
+    assert rel_err(one[1][rows], yc) <= TOL_BF16
+    assert rel_err(one[0], yr) <= TOL_BF16

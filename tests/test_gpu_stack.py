@@ -289,3 +289,41 @@ def test_two_lane_full_size_matches_serial_bitwise():
     for key in ("y_c", "y_r", "logits"):
         if a[key] is not None:
             assert np.array_equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------------ one launch per GLM linear
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_fused_glm_mode_matches_serial_bitwise_small(k):
+    """ROCS_EXEC_SHARED_FUSED on the small configs (their linears mostly stay
+    two launches: fewer than 2,048 candidates) gives the serial bits."""
+    from request_candidate_sharing_amd import rocs as R
+
+    inp = S.make_inputs(S.small_config(k))
+    _, a = _stack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    _, b = _stack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    for key in ("y_c", "y_r", "logits"):
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("k", [2, 4, 5])
+def test_fused_glm_mode_full_size_matches_serial_bitwise(k):
+    """Full-size stacks whose GLM linears run as one launch (the GLM MLP
+    stack's six linears, the Wukong-style and ranking stacks' MLPs):
+    identical bits to the serial schedule, twice in a row on one workspace."""
+    from request_candidate_sharing_amd import rocs as R
+    from request_candidate_sharing_amd.stacks import DeviceStack
+
+    inp = S.make_inputs(S.config(k))
+    fu = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    ser = DeviceStack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    ser.run()
+    b = ser.outputs()
+    for i in range(2):
+        fu.run()
+        a = fu.outputs()
+        for key in ("y_c", "y_r", "logits"):
+            if a[key] is not None:
+                assert np.array_equal(a[key], b[key]), (i, key)
