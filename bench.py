@@ -186,7 +186,7 @@ ROOFLINE_KERNEL = ("gemm_bf16_big_kernel<256, 256, 2, 4, 2> via rocs_lcb_candida
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_candidate_gemm_ranking_stack.json")
 # sources the candidate GEMM is compiled from (the counters are void once any of them changes)
 GEMM_SRCS = [os.path.join(ROOT, "request_candidate_sharing_amd", "csrc", f)
-             for f in ("rocs_gemm.hip", "rocs_mfma.h", "rocs_device.h")]
+             for f in ("rocs_gemm.hip", "rocs_gemm_tile.inc", "rocs_mfma.h", "rocs_device.h")]
 
 
 def gemm_source_sha():
