@@ -17,6 +17,7 @@ rate on a bounded sample of the same batch.
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -535,17 +536,25 @@ def fused_glm_study(args):
 
     cfg = S.config(2)
     inp = S.make_inputs(cfg)
-    B_r, B_c = cfg.B, int(len(inp["cand2req"]))
-    off = torch.as_tensor(inp["offsets"], device="cuda")
-    c2r = torch.as_tensor(inp["cand2req"], device="cuda")
-    batch = R.batch(B_r, B_c, off, c2r)
+    B_r = cfg.B
     g = torch.Generator(device="cuda").manual_seed(7)
     bf = torch.bfloat16
     rn = lambda *sh, sc=1.0: (torch.randn(*sh, device="cuda", generator=g) * sc).to(bf)
     st = R.cur_stream()
     ws = torch.empty(R.rocs_lcb_fused_workspace_size(B_r), dtype=torch.uint8, device="cuda")
-    for name, K, N, act, res in (("up 512 -> 1024, ReLU", 512, 1024, R.ROCS_ACT_RELU, False),
-                                 ("down 1024 -> 512, residual", 1024, 512, R.ROCS_ACT_NONE, True)):
+    # the stack's batch, then 100 and 10 candidates per request (grids of about
+    # four rounds of CUs, then less than one)
+    batches = [("U{64..512} per request", inp["cand2req"])]
+    for n in (100, 10):
+        batches.append(("%d per request" % n, np.repeat(np.arange(B_r, dtype=np.int32), n)))
+    for (bname, c2r_np), (name, K, N, act, res) in itertools.product(
+            batches, (("up 512 -> 1024, ReLU", 512, 1024, R.ROCS_ACT_RELU, False),
+                      ("down 1024 -> 512, residual", 1024, 512, R.ROCS_ACT_NONE, True))):
+        B_c = int(len(c2r_np))
+        counts = np.bincount(c2r_np, minlength=B_r)
+        off = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+        c2r = torch.as_tensor(np.ascontiguousarray(c2r_np, dtype=np.int32), device="cuda")
+        batch = R.batch(B_r, B_c, off, c2r)
         x_r, x_c = rn(B_r, K), rn(B_c, K)
         w_rr, w_cr, w_cc = rn(N, K, sc=K ** -0.5), rn(N, K, sc=K ** -0.5), rn(N, K, sc=K ** -0.5)
         b_r, b_c = rn(N, sc=0.5), rn(N, sc=0.5)
@@ -572,7 +581,7 @@ def fused_glm_study(args):
             torch.cuda.synchronize()
             outs[mode] = (e0.elapsed_time(e1) * 1e3 / reps, y_r.clone(), y_c.clone(), z.clone())
         same = all(torch.equal(outs["two"][i], outs["one"][i]) for i in (1, 2, 3))
-        print(json.dumps({"study": "fused_glm", "layer": name, "B_r": B_r, "B_c": B_c,
+        print(json.dumps({"study": "fused_glm", "layer": name, "candidates": bname, "B_r": B_r, "B_c": B_c,
                           "two_launches_us": outs["two"][0], "one_launch_us": outs["one"][0],
                           "same_bits": bool(same)}), flush=True)
 
