@@ -137,7 +137,9 @@ int rocs_lcb_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r,
  * take the lowest workgroup ids; a candidate tile polls the counters of the
  * 32-row request blocks its map entries name before it reads z.  A poll
  * gives up after a bounded number of tries (it cannot be reached while
- * workgroups dispatch in id order); the tile's outputs are then NaN.
+ * workgroups dispatch in id order); the tile's accumulators are then NaN
+ * (NaN outputs, zeros after ReLU) and the int after the counters, at int
+ * index (B_r + 31) / 32 of the workspace, is set to 1 (the call clears it).
  * Returns ROCS_ERR_UNSUPPORTED, having enqueued nothing, unless dtype is
  * bf16, 0 < B_r < 2048, B_c >= 2048, d_out_c > 128 and a multiple of 256,
  * at most one of ReLU and res_c is used, and every row offset of y_c, res_c
@@ -344,8 +346,8 @@ typedef enum rocs_exec_mode {
  * workgroup ids (dispatched first, they wait for nothing); a candidate tile
  * polls one completion counter per 32 request rows it reads, in the
  * workspace, zeroed once at the start of the call.  A poll gives up after a
- * bounded number of tries; the tile's outputs are then NaN.  Outputs are
- * bit-identical to ROCS_EXEC_SHARED_SERIAL. */
+ * bounded number of tries; the tile's accumulators are then NaN.  Outputs
+ * are bit-identical to ROCS_EXEC_SHARED_SERIAL. */
 /* Schedule of ROCS_EXEC_SHARED with both row groups present and a DCA
  * descriptor of more than one depth ([R] §2.4: the request and candidate
  * tiles share the GPU, the dependency on the request contribution is a

@@ -10,7 +10,7 @@
 // Workgroups are dispatched in id order, so a candidate tile that is running
 // has every request tile already dispatched, and request tiles wait for
 // nothing: every wait ends.  A wait is bounded all the same (kSpinLimit
-// polls); one that gives up sets *err and lets the tile go on.
+// polls); one that gives up sets *err and the tile writes NaN.
 //
 // Counters.  One int per 32-row block of request rows counts the request
 // tiles of that block that have stored their outputs (`target` of them
@@ -27,13 +27,15 @@
 // quarters (32 x 32 tiles on four waves); the candidate tiles run the
 // candidate launch's tile plan with its accumulators started at Z.  Every
 // output is bit-identical to the two-launch path.
+#include <cstdlib>
+
 #include "rocs_gemm_tile.inc"
 
 namespace rocs {
 
 namespace {
 
-constexpr int kSpinLimit = 1 << 18;
+constexpr int kSpinLimit = 1 << 18;  // polls of one counter before a wait gives up
 
 struct FusedArgs {
   GemmArgs req, cand;
@@ -44,6 +46,7 @@ struct FusedArgs {
   int target;    // request tiles that cover one 32-row block
   int rblocks;   // 32-row blocks of request rows
   int M1;        // mixed candidate plan: rows in 256-row tiles
+  int polls;     // polls of one counter before a wait gives up
 };
 
 // The candidate tile's wait: the request rows it reads are those its map
@@ -53,7 +56,7 @@ struct ZRowsReady {
   const int32_t* zmap;
   int M, zrows;
   const int* flags;
-  int target;
+  int target, polls;
   int* err;
   __device__ __forceinline__ bool operator()(int m0, int rows) const {
     __shared__ int ready_s;
@@ -78,9 +81,9 @@ struct ZRowsReady {
       if (lane == 0) {
         bool gave_up = false;
         for (int rb = lo >> 5; rb <= (hi >> 5) && !gave_up; ++rb) {  // none when hi < 0
-          int polls = 0;
+          int n_polls = 0;
           while (__hip_atomic_load(flags + rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++polls > kSpinLimit) {
+            if (++n_polls > polls) {
               __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               gave_up = true;
               break;
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(512, 1) void glm_fused_kernel(FusedArgs f) {
     return;
   }
   const GemmArgs& a = f.cand;
-  const ZRowsReady ready{a.zmap, a.M, a.zrows, f.flags, f.target, f.err};
+  const ZRowsReady ready{a.zmap, a.M, a.zrows, f.flags, f.target, f.polls, f.err};
   const int cb = b - f.req_wg, nc = gridDim.x - f.req_wg;
   const int ntn = (a.N + 255) / 256;
   if constexpr (H2 == 0) {
@@ -201,6 +204,17 @@ hipError_t launch_glm_fused(DType dt, const GemmArgs& req, const GemmArgs& cand,
     f.req_kind = 0;
     f.req_wg = ((req.M + 63) / 64) * ((req.N + 127) / 128);
     f.target = (req.N + 127) / 128;
+  }
+  f.polls = kSpinLimit;
+  // Failure injection for tests of the bounded wait: ROCS_TEST_FUSED_GIVE_UP=n
+  // sets a target no counter reaches and n polls, so every candidate tile
+  // gives up after n polls (its outputs NaN, *err set) and the grid drains.
+  if (const char* e = std::getenv("ROCS_TEST_FUSED_GIVE_UP")) {
+    const int n = std::atoi(e);
+    if (n > 0) {
+      f.polls = n;
+      f.target = 0x7fffffff;
+    }
   }
   const int ntn = (cand.N + 255) / 256;
   const CandPlan p = cand_plan(cand.M, ntn);

@@ -223,3 +223,32 @@ def test_fused_glm_full_size_glm_mlp_shapes(layer):
     yr, yc = c.oracle(rows)
     assert rel_err(one[1][rows], yc) <= TOL_BF16
     assert rel_err(one[0], yr) <= TOL_BF16
+
+
+@pytest.mark.parametrize("ci", [1, 4])
+def test_fused_glm_wait_gives_up_cleanly(monkeypatch, ci):
+    """Failure injection from the host (ROCS_TEST_FUSED_GIVE_UP: a counter
+    target no request tile reaches, 8 polls): every candidate tile gives up
+    with NaN accumulators (NaN outputs; zeros after a ReLU) and sets the
+    error word after the counters, the request outputs and Z are those of the
+    two-launch path, and the grid drains, so the next call is right and
+    leaves the error word clear."""
+    c = _make(CASES[ci])
+    two, _ = c.both()
+    monkeypatch.setenv("ROCS_TEST_FUSED_GIVE_UP", "8")
+    _, (y_r, y_c, z) = c.run(True)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("ROCS_TEST_FUSED_GIVE_UP")
+    got = to_np(y_c)
+    if c.act == _R().ROCS_ACT_RELU:
+        assert (got == 0).all()
+    else:
+        assert np.isnan(got).all()
+    assert np.array_equal(to_np(y_r), two[0])
+    assert np.array_equal(to_np(z), two[2])
+    err_at = (c.B + 31) // 32
+    assert c.ws.view(torch.int32)[err_at].item() == 1
+    two, one = c.both()
+    for a, b in zip(two, one):
+        assert np.array_equal(a, b, equal_nan=True)
+    assert c.ws.view(torch.int32)[err_at].item() == 0
