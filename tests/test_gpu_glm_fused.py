@@ -131,6 +131,13 @@ CASES = [
     dict(counts=("r", 200, 26), dims=(512, 512, 512, 1024), act=1, seed=34, shuffle=True),
     # one request, many candidates; empty-request neighbours
     dict(counts=[0, 2600, 0], dims=(64, 128, 64, 512), act=1, seed=35),
+    # the other candidate tile plans, each with another epilogue variant:
+    # 256-row tiles throughout (65,536 rows, N = 256; bias only)
+    dict(counts=[16384] * 4, dims=(64, 64, 64, 256), act=0, seed=40),
+    # a round of 256-row tiles, then 64-row tiles (70,536 rows, N = 256; ReLU, no bias)
+    dict(counts=[17634] * 4, dims=(64, 64, 64, 256), act=1, seed=41, bias=False),
+    # a round of 256-row tiles, then 192-row tiles (26,384 rows, N = 1024; residual, no bias)
+    dict(counts=[6596] * 4, dims=(128, 128, 64, 1024), act=0, seed=42, bias=False, res=True),
 ]
 
 
@@ -138,7 +145,8 @@ def _make(c):
     counts = c["counts"]
     if counts[0] == "r":
         counts = _counts(np.random.default_rng(c["seed"]), counts[1], counts[2])
-    return Case(counts, *c["dims"], c["act"], c["seed"], res=c.get("res", False), shuffle=c.get("shuffle", False))
+    return Case(counts, *c["dims"], c["act"], c["seed"], res=c.get("res", False), bias=c.get("bias", True),
+                shuffle=c.get("shuffle", False))
 
 
 @pytest.mark.parametrize("ci", range(len(CASES)))
@@ -152,7 +160,7 @@ def test_fused_glm_bit_identical_to_two_launches(ci):
     assert np.isfinite(one[1]).all()
 
 
-@pytest.mark.parametrize("ci", [0, 1, 3])
+@pytest.mark.parametrize("ci", [0, 1, 3, 5, 6, 7])
 def test_fused_glm_matches_oracle(ci):
     c = _make(CASES[ci])
     _, (y_r, y_c, z) = c.run(True)
