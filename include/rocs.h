@@ -140,10 +140,15 @@ int rocs_lcb_forward(const rocs_batch* batch, rocs_dtype dtype, const void* x_r,
  * workgroups dispatch in id order); the tile's accumulators are then NaN
  * (NaN outputs, zeros after ReLU) and the int after the counters, at int
  * index (B_r + 31) / 32 of the workspace, is set to 1 (the call clears it).
+ * Tests force that path from the host: with the environment variable
+ * ROCS_TEST_FUSED_GIVE_UP=n (n > 0) the call waits for a count no request
+ * tile reaches and gives up after n polls per candidate tile.
  * Returns ROCS_ERR_UNSUPPORTED, having enqueued nothing, unless dtype is
  * bf16, 0 < B_r < 2048, B_c >= 2048, d_out_c > 128 and a multiple of 256,
  * at most one of ReLU and res_c is used, and every row offset of y_c, res_c
- * and z fits in 31 bits. */
+ * and z fits in 31 bits; ROCS_ERR_WORKSPACE for a short or NULL workspace. */
+/* Workspace bytes of rocs_lcb_forward_fused: (B_r + 31) / 32 completion
+ * counters and the error word, as ints, rounded up to 256 bytes. */
 size_t rocs_lcb_fused_workspace_size(int32_t B_r);
 int rocs_lcb_forward_fused(const rocs_batch* batch, rocs_dtype dtype, const void* x_r, int64_t ld_xr,
                            int32_t d_in_r, const void* x_c, int64_t ld_xc, int32_t d_in_c, const void* w_rr,
