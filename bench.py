@@ -586,6 +586,39 @@ def fused_glm_study(args):
                           "same_bits": bool(same)}), flush=True)
 
 
+def blas_reference_study(args):
+    """Context only, not the product path: the vendor GEMM (torch.mm, which
+    dispatches to hipBLASLt) on the candidate GEMM shapes of the stacks,
+    without the fused request-contribution epilogue, and a large square GEMM
+    for the practical bf16 rate of the part.  Operands stay resident (the
+    same buffers every launch)."""
+    import torch
+
+    shapes = [("ranking stack MLP1", 32486, 1024, 2048), ("ranking stack layer-1 MLP1", 32486, 512, 2048),
+              ("ranking stack MLP2", 32486, 2048, 512), ("GLM MLP stack up", 73704, 512, 1024),
+              ("GLM MLP stack down", 73704, 1024, 512), ("Wukong-style MLP1", 30231, 8960, 1024),
+              ("square", 8192, 8192, 8192)]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, M, K, N in shapes:
+        x = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        wt = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(args.warmup):
+            torch.mm(x, wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(args.steps, 30)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(x, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"study": "blas_reference", "shape": name, "M": M, "K": K, "N": N, "us": us,
+                          "tflops": 2.0 * M * N * K / us / 1e6, "frac": 2.0 * M * N * K / us / 1e6 / 2500.0}),
+              flush=True)
+        del x, wt
+
+
 def w8a16_study(args):
     """Latency of the W8A16 linear layer against the bf16 GEMM of the same
     shape, at the layer shapes of the UG-Separation page's W8A16 table.
@@ -705,6 +738,8 @@ def main():
                     help="the UG-Separation TokenMixer workload (shared vs dense comparator), one JSON line")
     ap.add_argument("--w8a16", action="store_true",
                     help="W8A16 linear vs the bf16 GEMM at the UG-Separation page's W8A16 shapes, one JSON line each")
+    ap.add_argument("--blas-ref", action="store_true",
+                    help="context: the vendor GEMM (torch.mm) on the stacks' candidate GEMM shapes, no epilogue")
     ap.add_argument("--fused-glm", action="store_true",
                     help="study: a GLM linear as one launch vs two launches (GLM MLP stack shapes)")
     ap.add_argument("--order", action="store_true",
@@ -744,6 +779,8 @@ def main():
         return w8a16_study(args)
     if args.fused_glm:
         return fused_glm_study(args)
+    if args.blas_ref:
+        return blas_reference_study(args)
     if args.workload != 5:
         return other_workload(args)
 
