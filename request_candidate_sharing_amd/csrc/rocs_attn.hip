@@ -10,8 +10,11 @@
 // stored (row-major key rows), global -> LDS by DMA through a 3-stage ring
 // (two slabs in flight).  Each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, so each lane holds scores of a single query:
-// the online-softmax max/sum need one exchange between lanes l and l ^ 32
-// per slab (v_permlane32_swap).  P^T is fed back as the B operand of
+// the online-softmax max needs one exchange between lanes l and l ^ 32 per
+// slab (v_permlane32_swap).  The row sums of P come from the matrix cores:
+// one more 32 x 32 accumulator takes ones x P^T next to the PV product, so
+// every register of lane l holds the sum of its query's bf16 P (the
+// softmax is VALU-issue bound and the MFMA pipe has room).  P^T is fed back as the B operand of
 // O^T = V^T P^T in the register order the S^T accumulator produced; the
 // V^T operand is read from the row-major value tile with transposing LDS
 // reads (ds_read_b64_tr_b16) in that same key order.  Softmax in fp32 with
@@ -24,7 +27,6 @@ namespace rocs {
 
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One wave-instruction of global -> LDS DMA: lane i's 16 bytes land at
@@ -117,7 +119,8 @@ __device__ __forceinline__ bool decode_tile(const AttnArgs& a, QTile& t) {
 struct QState {
   bf16x8 qf[4];
   f32x16 o_acc[2];
-  float m_run, l_run;
+  f32x16 l_acc;  // every register: the running sum of this lane's query's P
+  float m_run;
 };
 
 // Candidates whose request id was out of range get NaN rows.
@@ -138,19 +141,16 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int64_t q_phys, bool q
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int j = 0; j < 16; ++j) st.o_acc[t][j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.l_acc[j] = 0.f;
   st.m_run = -INFINITY;
-  st.l_run = 0.f;
 }
 
-// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap gives every lane
-// both values: a VALU exchange, no LDS round trip).
+// max of x over lanes l and l ^ 32 (v_permlane32_swap gives every lane both
+// values: a VALU exchange, no LDS round trip).
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -241,7 +241,8 @@ __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, in
   if (__builtin_amdgcn_ballot_w64((mx - st.m_run) * c > 8.f)) {
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);  // 0 on the first slab
-    st.l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.l_acc[j] *= alpha;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -249,23 +250,13 @@ __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, in
     st.m_run = m_new;
   }
   const float mc = st.m_run * c;
-  float psum = 0.f;
   bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
+    for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pf[kt * 2 + sp][q] = to_bf(__builtin_amdgcn_exp2f(fmaf(s[kt][sp * 8 + q], c, -mc)));
-      // l sums the bf16 P the PV product uses, two at a time (v_dot2_f32_bf16 with ones)
-#pragma unroll
-      for (int q = 0; q < 8; q += 2) {
-        const bf16x2 pp = {pf[kt * 2 + sp][q], pf[kt * 2 + sp][q + 1]};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{to_bf(1.f), to_bf(1.f)}, psum, false);
-      }
-    }
-  psum = halves_sum(psum);
-  st.l_run += psum;
 
   // O^T[dh][query] += V^T[dh][keys] P^T[keys][query]
 #pragma unroll
@@ -276,10 +267,16 @@ __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, in
       for (int sp = 0; sp < 2; ++sp)
         st.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[dt * 4 + kt * 2 + sp]),
                                                                pf[kt * 2 + sp], st.o_acc[dt], 0, 0, 0);
+  // l += ones x P^T: the sum over the slab's 64 keys of the bf16 P the PV
+  // product uses, for this lane's query, in every register
+  const bf16 one = to_bf(1.f);
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[t], st.l_acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t q_phys, int h, int hl, const QState& st) {
-  const float inv = 1.0f / st.l_run;
+  const float inv = 1.0f / st.l_acc[0];
   bf16* o = a.o + q_phys * a.ldo + h * DH;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
