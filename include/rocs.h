@@ -351,8 +351,12 @@ typedef enum rocs_exec_mode {
  * workgroup ids (dispatched first, they wait for nothing); a candidate tile
  * polls one completion counter per 32 request rows it reads, in the
  * workspace, zeroed once at the start of the call.  A poll gives up after a
- * bounded number of tries; the tile's accumulators are then NaN.  Outputs
- * are bit-identical to ROCS_EXEC_SHARED_SERIAL. */
+ * bounded number of tries; the tile's accumulators are then NaN.  The
+ * candidate cross-attention (the persistent attention kernel of §2.4) runs
+ * on one round of workgroups, three per compute unit, each walking the
+ * (query tile, head) pairs of its XCD's range; test variable
+ * ROCS_TEST_ATTN_ROUND=n sets that round to n workgroups (a multiple of 8).
+ * Outputs are bit-identical to ROCS_EXEC_SHARED_SERIAL. */
 /* Schedule of ROCS_EXEC_SHARED with both row groups present and a DCA
  * descriptor of more than one depth ([R] §2.4: the request and candidate
  * tiles share the GPU, the dependency on the request contribution is a

@@ -481,9 +481,10 @@ int xattn_request_launch(int B_r, int H, int L, const void* q_r, int64_t ld_qr, 
 // with a plan: per-request query tiles (shared execution); without: one group per candidate
 int xattn_candidate_launch(int B_r, int B_c, const XattnPlan& plan, int H, int L, const void* q_c, int64_t ld_qc,
                            const void* k_c, const void* v_c, int64_t ld_kv, int64_t kv_group_stride, float scale_log2,
-                           void* a_c, int64_t ld_ac, hipStream_t s) {
+                           void* a_c, int64_t ld_ac, hipStream_t s, bool persistent = false) {
   if (B_c == 0) return ROCS_OK;
   AttnArgs at{};
+  at.persistent = persistent ? 1 : 0;
   at.n_heads = H;
   at.L = L;
   at.q = reinterpret_cast<const bf16*>(q_c);

@@ -21,6 +21,7 @@
 // exp2 and the scale folded into one multiply-add; the running maximum is
 // only moved when a score exceeds it by more than 2^8 in exp2 units (lazy
 // rescaling).
+#include <cstdlib>
 #include "rocs_device.h"
 
 namespace rocs {
@@ -88,15 +89,21 @@ __device__ __forceinline__ int k_off(int key, int chunk) { return key * 8 + (chu
 struct QTile {
   int group, rbeg, rend, h;
 };
-__device__ __forceinline__ bool decode_tile(const AttnArgs& a, QTile& t) {
+// (tile, head) pairs of a launch: tiles of the plan (or of the uniform
+// groups) times heads; a plan's count is an upper bound (max_tiles).
+__device__ __forceinline__ int attn_total(const AttnArgs& a) {
+  const int tiles = a.q_rows_per_group > 0 ? a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ) : a.max_tiles;
+  return tiles * a.n_heads;
+}
+
+// Tile and head of logical pair `logical`; false past the plan's tile count.
+__device__ __forceinline__ bool decode_tile(const AttnArgs& a, int logical, QTile& t) {
   const int H = a.n_heads;
   int n_tiles;
   if (a.q_rows_per_group > 0)
     n_tiles = a.n_groups * ((a.q_rows_per_group + TQ - 1) / TQ);
   else
     n_tiles = *a.n_tiles_dev;
-  const int total = (a.q_rows_per_group > 0 ? n_tiles : a.max_tiles) * H;
-  const int logical = xcd_remap(blockIdx.x, total);
   const int tile = logical / H;
   t.h = logical - tile * H;
   if (tile >= n_tiles) return false;
@@ -302,11 +309,12 @@ struct Stage {
 };
 constexpr int DMA_PER_SLAB = 4;  // wave-instructions per slab per wave (2 K + 2 V)
 
-__global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
-  __shared__ uint4 sK[NST][KC * 8];
-  __shared__ uint4 sV[NST][KC * 8];
+typedef uint4 AttnRing[NST][KC * 8];
+
+// One (tile, head) pair on the workgroup's K and V rings.
+__device__ __forceinline__ void attn_tile(const AttnArgs& a, int logical, AttnRing& sK, AttnRing& sV) {
   QTile t;
-  if (!decode_tile(a, t)) return;
+  if (!decode_tile(a, logical, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q_local = t.rbeg + wave * 32 + (lane & 31);
@@ -387,6 +395,32 @@ __global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
   }
   wait_vmcnt<0>();  // no DMA may still write this workgroup's LDS when it exits
   if (q_ok) write_out(a, q_phys, t.h, hl, st);
+}
+
+__global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
+  __shared__ AttnRing sK, sV;
+  attn_tile(a, xcd_remap(blockIdx.x, attn_total(a)), sK, sV);
+}
+
+// The persistent grid ([R] §2.4, the persistent attention kernel across short
+// query tiles): one round of workgroups (three per CU), each walking the
+// (tile, head) pairs of its XCD's contiguous range, the range the one-pair-
+// per-workgroup grid gives that XCD, so a request's tiles still share that
+// XCD's L2.  The rings and the lane-constant DMA and read offsets are reused
+// from pair to pair; a barrier separates pairs (a fast wave may not refill a
+// stage that a slow wave still reads).  Every pair is computed as in
+// attn_dma_kernel, so the outputs are the same bits.
+__global__ __launch_bounds__(256, 3) void attn_persist_kernel(AttnArgs a) {
+  __shared__ AttnRing sK, sV;
+  const int total = attn_total(a);
+  const int q = total >> 3, r = total & 7;
+  const int x = blockIdx.x & 7, px = gridDim.x >> 3;  // gridDim.x is a multiple of 8
+  const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  const int size = q + (x < r ? 1 : 0);
+  for (int k = blockIdx.x >> 3; k < size; k += px) {
+    if (k >= px) __syncthreads();
+    attn_tile(a, start + k, sK, sV);
+  }
 }
 
 // ----------------------------------------------------------------- planning
@@ -610,7 +644,19 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.L <= 0) return hipErrorInvalidValue;
   // the kernel addresses 64 key rows by 32-bit byte offsets
   if (a.ldkv >= kMaxAttnLdkv) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_dma_kernel, dim3(tiles * a.n_heads), dim3(256), 0, s, a);
+  const int total = tiles * a.n_heads;
+  int round = 3 * device_cus() / 8 * 8;  // three workgroups per CU, a multiple of the 8 XCDs
+  // For tests of the pair walk at small sizes: ROCS_TEST_ATTN_ROUND=n sets a
+  // round of n workgroups (rounded down to a multiple of 8).
+  if (a.persistent)
+    if (const char* e = std::getenv("ROCS_TEST_ATTN_ROUND")) {
+      const int n = std::atoi(e) / 8 * 8;
+      if (n >= 8) round = n;
+    }
+  if (a.persistent && total > round && round >= 8)
+    hipLaunchKernelGGL(attn_persist_kernel, dim3(round), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_dma_kernel, dim3(total), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

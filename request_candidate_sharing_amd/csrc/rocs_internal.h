@@ -69,6 +69,8 @@ __host__ __device__ inline GemmArgs batch_slice(const GemmArgs& a, int i) {
 }
 
 hipError_t launch_gemm(DType dt, const GemmArgs& a, hipStream_t s);
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus();
 // Launch choices of launch_gemm, by shape: the epilogue variant, whether a
 // launch of fewer than 2,048 rows splits K, and the candidate tile plan.
 int epilogue_variant(const GemmArgs& a);
@@ -165,6 +167,7 @@ struct AttnArgs {
   const int32_t* n_tiles_dev;
   const int32_t* perm;  // optional row permutation: logical row r is physical row perm[r]
   int max_tiles;
+  int persistent;  // 1: one round of workgroups walks the (tile, head) pairs (same bits)
 };
 // hipErrorInvalidValue when ldkv >= 2^24 (64 key rows are addressed by
 // 32-bit byte offsets) or L <= 0

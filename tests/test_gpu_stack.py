@@ -307,6 +307,24 @@ def test_fused_glm_mode_matches_serial_bitwise_small(k):
             assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("k", [3, 5])
+@pytest.mark.parametrize("round_wg", [8, 16])
+def test_fused_mode_persistent_attention_walk_small(k, round_wg, monkeypatch):
+    """ROCS_EXEC_SHARED_FUSED runs the candidate cross-attention on one round
+    of workgroups that walk the (tile, head) pairs; a round of 8 or 16
+    workgroups (test variable) makes each walk several pairs, ragged over the
+    XCD ranges and past the plan's tile count: the serial bits."""
+    from request_candidate_sharing_amd import rocs as R
+
+    inp = S.make_inputs(S.small_config(k))
+    _, b = _stack(inp, mode=R.ROCS_EXEC_SHARED_SERIAL)
+    monkeypatch.setenv("ROCS_TEST_ATTN_ROUND", str(round_wg))
+    _, a = _stack(inp, mode=R.ROCS_EXEC_SHARED_FUSED)
+    for key in ("y_c", "y_r", "logits"):
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("k", [2, 4, 5])
 def test_fused_glm_mode_full_size_matches_serial_bitwise(k):
