@@ -403,10 +403,13 @@ __global__ __launch_bounds__(256, 3) void attn_dma_kernel(AttnArgs a) {
 // query tiles): one round of workgroups (three per CU), each walking the
 // (tile, head) pairs of its XCD's contiguous range, the range the one-pair-
 // per-workgroup grid gives that XCD, so a request's tiles still share that
-// XCD's L2.  The rings and the lane-constant DMA and read offsets are reused
-// from pair to pair; a barrier separates pairs (a fast wave may not refill a
-// stage that a slow wave still reads).  Every pair is computed as in
-// attn_dma_kernel, so the outputs are the same bits.
+// XCD's L2.  The workgroup's LDS rings are reused from pair to pair; a
+// barrier separates pairs (a fast wave may not refill a stage that a slow
+// wave still reads).  Every pair is computed as in attn_dma_kernel, so the
+// outputs are the same bits.  Measured slower than one workgroup per pair on
+// the ranking-scale stack (the barrier holds all four waves until the
+// slowest ends the pair, where a new workgroup would start beside the CU's
+// other two), so only the one-launch schedule uses it.
 __global__ __launch_bounds__(256, 3) void attn_persist_kernel(AttnArgs a) {
   __shared__ AttnRing sK, sV;
   const int total = attn_total(a);
