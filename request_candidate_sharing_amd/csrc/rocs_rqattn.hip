@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void rq_fold_kernel(RqAttnArgs a) {
 // contributions p S_l to u then run on the VALU with a lane owning H
 // consecutive features (the rows are read again, from L2).
 template <int H>
-__global__ __launch_bounds__(256) void rq_attend_kernel(RqAttnArgs a) {
+__global__ __launch_bounds__(256, 2) void rq_attend_kernel(RqAttnArgs a) {
   constexpr int D = 64 * H;
   constexpr int KB = D / 32;  // 32-wide K steps
   using Frag = typename RowFrag<H>::T;
@@ -217,22 +217,34 @@ __global__ __launch_bounds__(256) void rq_attend_kernel(RqAttnArgs a) {
   }
   __syncthreads();
 
-  float m[H], l[H], u[H][H];
+  // p = 2^(s - m_h) of the wave's events, each (event, head) once per wave
+  // and in place (every lane needs all of them below); events past L have
+  // score -inf (p = 0) and zero rows: they add nothing
+#pragma unroll
+  for (int t = 0; t < (RQ_WROWS * H + 63) / 64; ++t) {
+    const int i = lane + 64 * t;
+    if (i < RQ_WROWS * H) {
+      const int j = i / H, h = i - (i / H) * H;
+      float& e = sc[wave * RQ_WROWS + j][h];
+      e = __builtin_amdgcn_exp2f(e - mx[h]);  // argument <= 0
+    }
+  }
+  __syncthreads();
+
+  float l[H], u[H][H];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    m[h] = mx[h];
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < H; ++e) u[h][e] = 0.f;
   }
-  // events past L have score -inf (p = 0) and zero rows: they add nothing
 #pragma unroll
   for (int j = 0; j < RQ_WROWS; ++j) {
     float x[H];
     unpack_row<H>(rows[j], x);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const float p = __builtin_amdgcn_exp2f(sc[wave * RQ_WROWS + j][h] - m[h]);  // argument <= 0
+      const float p = sc[wave * RQ_WROWS + j][h];
       l[h] += p;
 #pragma unroll
       for (int e = 0; e < H; ++e) u[h][e] = fmaf(p, x[e], u[h][e]);
