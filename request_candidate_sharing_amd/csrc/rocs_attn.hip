@@ -225,58 +225,61 @@ __device__ __forceinline__ void attend_slab(const uint4* tK, const uint4* tV, in
         vf[dt * 4 + kt * 2 + sp] = __builtin_bit_cast(uint4, v8s(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
       }
   __builtin_amdgcn_sched_barrier(0);
-  // The slab's two 32-key halves in turn: the second half's scores are still
-  // in the matrix core while the first half's exponentials run, and the
-  // first half's PV products while the second half's run.  Each half updates
-  // the reference on its own (keys beyond L, last slab only, score -inf).
-  const bf16 one = to_bf(1.f);
-  const bf16x8 ones = {one, one, one, one, one, one, one, one};
-  bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
+  // mask keys beyond L (last slab only)
+  if (key0 + KC > L) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    if (key0 + KC > L) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = key0 + kt * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
         if (key >= L) s[kt][j] = -INFINITY;
       }
-    }
-    float mx = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
-    mx = halves_max(mx);
-    // Lazy rescaling: the running reference m_run moves only when some query
-    // of the wave sees a score more than 2^8 above it (in exp2 units);
-    // otherwise P may reach 2^8, which fp32 sums and bf16 P hold as well as
-    // values <= 1.  O and l always share one reference, so O / l is unchanged.
-    if (__builtin_amdgcn_ballot_w64((mx - st.m_run) * c > 8.f)) {
-      const float m_new = fmaxf(st.m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);  // 0 on the first slab
+  mx = halves_max(mx);
+  // Lazy rescaling: the running reference m_run moves only when some query of
+  // the wave sees a score more than 2^8 above it (in exp2 units); otherwise
+  // P may reach 2^8, which fp32 sums and bf16 P hold as well as values <= 1.
+  // O and l always share one reference, so O / l is unchanged.
+  if (__builtin_amdgcn_ballot_w64((mx - st.m_run) * c > 8.f)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);  // 0 on the first slab
 #pragma unroll
-      for (int j = 0; j < 16; ++j) st.l_acc[j] *= alpha;
+    for (int j = 0; j < 16; ++j) st.l_acc[j] *= alpha;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) st.o_acc[t][j] *= alpha;
-      st.m_run = m_new;
-    }
-    const float mc = st.m_run * c;
+      for (int j = 0; j < 16; ++j) st.o_acc[t][j] *= alpha;
+    st.m_run = m_new;
+  }
+  const float mc = st.m_run * c;
+  bf16x8 pf[4];  // B operand for the PV step: [kt*2 + step]
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pf[kt * 2 + sp][q] = to_bf(__builtin_amdgcn_exp2f(fmaf(s[kt][sp * 8 + q], c, -mc)));
-    // O^T[dh][query] += V^T[dh][keys] P^T[keys][query]; l += ones x P^T (the
-    // sum of the bf16 P the PV product uses, for this lane's query, in every
-    // register)
+
+  // O^T[dh][query] += V^T[dh][keys] P^T[keys][query]
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
         st.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[dt * 4 + kt * 2 + sp]),
                                                                pf[kt * 2 + sp], st.o_acc[dt], 0, 0, 0);
-      st.l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[kt * 2 + sp], st.l_acc, 0, 0, 0);
-    }
-  }
+  // l += ones x P^T: the sum over the slab's 64 keys of the bf16 P the PV
+  // product uses, for this lane's query, in every register
+  const bf16 one = to_bf(1.f);
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[t], st.l_acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t q_phys, int h, int hl, const QState& st) {
